@@ -1,0 +1,279 @@
+"""Python binding of libxfer (include/xfer.h): argument marshalling only.
+
+Every step of the path runs in the HIP library; this module turns torch
+tensors and numpy arrays into pointers and sizes, passes the current torch
+stream, and raises XferError on a non-OK status.  It has no fallback: if
+libxfer.so is missing, importing the functions fails loudly.
+
+Device buffers are torch CUDA tensors (PyTorch supplies memory and streams);
+run tables and addresses are numpy arrays on the host.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libxfer.so")
+
+OK, E_INVAL, E_UNSUPPORTED, E_TABLE, E_RANGE, E_OVERLAP, E_DEVICE = range(7)
+OUT_F32, OUT_BF16 = 0, 1
+ARGMAX, TOP2 = 0, 1
+
+EXPORTED = [
+    "xfer_status_str", "xfer_pack_bf16", "xfer_combine2", "xfer_argmax_workspace_bytes",
+    "xfer_argmax_merge", "xfer_runs_encode", "xfer_runs_validate", "xfer_runs_plan_bytes",
+    "xfer_runs_prepare", "xfer_gather_runs", "xfer_scatter_runs",
+]
+
+
+class XferError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {status_str(status)} (status {status})")
+        self.status = status
+
+
+class Shard(ctypes.Structure):
+    _fields_ = [("ptr", ctypes.c_void_p), ("ld", ctypes.c_size_t), ("rows", ctypes.c_uint32),
+                ("ncols", ctypes.c_uint32), ("col_offset", ctypes.c_uint32)]
+
+
+class RunTableC(ctypes.Structure):
+    _fields_ = [("n_lanes", ctypes.c_uint32), ("n_blocks", ctypes.c_uint32), ("seg_bytes", ctypes.c_uint64),
+                ("n_runs", ctypes.c_uint64), ("runs_per_lane", ctypes.c_void_p), ("run_base", ctypes.c_void_p),
+                ("run_stride", ctypes.c_void_p), ("run_count", ctypes.c_void_p)]
+
+
+class Region(ctypes.Structure):
+    _fields_ = [("base", ctypes.c_uint64), ("bytes", ctypes.c_uint64)]
+
+
+class RunsPlan(ctypes.Structure):
+    _fields_ = [("dev", ctypes.c_void_p), ("dev_bytes", ctypes.c_uint64), ("n_lanes", ctypes.c_uint32),
+                ("n_blocks", ctypes.c_uint32), ("seg_bytes", ctypes.c_uint64), ("n_runs", ctypes.c_uint64),
+                ("span_lo", ctypes.c_uint64), ("span_hi", ctypes.c_uint64), ("is_dst", ctypes.c_uint32),
+                ("tile_blocks", ctypes.c_uint32), ("n_tiles", ctypes.c_uint32), ("magic", ctypes.c_uint32),
+                ("off_tile_run", ctypes.c_uint64), ("off_run_start", ctypes.c_uint64),
+                ("off_run_base", ctypes.c_uint64), ("off_run_stride", ctypes.c_uint64)]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libxfer.so (raises if it is not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        P, S, U32, U64, I = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_uint32, ctypes.c_uint64, ctypes.c_int
+        L.xfer_status_str.argtypes = [I]
+        L.xfer_status_str.restype = ctypes.c_char_p
+        L.xfer_pack_bf16.argtypes = [P, S, P, S, S, S, S, P]
+        L.xfer_pack_bf16.restype = I
+        L.xfer_combine2.argtypes = [P, P, S, P, I, P]
+        L.xfer_combine2.restype = I
+        L.xfer_argmax_workspace_bytes.argtypes = [U32, U32, U32]
+        L.xfer_argmax_workspace_bytes.restype = S
+        L.xfer_argmax_merge.argtypes = [ctypes.POINTER(Shard), ctypes.POINTER(Shard), I, P, P, S, P]
+        L.xfer_argmax_merge.restype = I
+        L.xfer_runs_encode.argtypes = [P, U32, U32, U32, P, P, P, P, U64, ctypes.POINTER(U64)]
+        L.xfer_runs_encode.restype = I
+        L.xfer_runs_validate.argtypes = [ctypes.POINTER(RunTableC), ctypes.POINTER(Region), I, I]
+        L.xfer_runs_validate.restype = I
+        L.xfer_runs_plan_bytes.argtypes = [ctypes.POINTER(RunTableC)]
+        L.xfer_runs_plan_bytes.restype = S
+        L.xfer_runs_prepare.argtypes = [ctypes.POINTER(RunTableC), ctypes.POINTER(Region), I, I, P, S,
+                                        ctypes.POINTER(RunsPlan)]
+        L.xfer_runs_prepare.restype = I
+        L.xfer_gather_runs.argtypes = [ctypes.POINTER(RunsPlan), P, S, P]
+        L.xfer_gather_runs.restype = I
+        L.xfer_scatter_runs.argtypes = [P, S, ctypes.POINTER(RunsPlan), P]
+        L.xfer_scatter_runs.restype = I
+        _lib = L
+    return _lib
+
+
+def status_str(status: int) -> str:
+    return lib().xfer_status_str(status).decode()
+
+
+def _check(status: int, what: str) -> None:
+    if status != OK:
+        raise XferError(status, what)
+
+
+def _stream(stream):
+    if stream is not None:
+        return int(stream)
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _dev(t) -> int:
+    """Pointer of a CUDA tensor (None -> NULL)."""
+    if t is None:
+        return 0
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError("expected a contiguous CUDA tensor")
+    return t.data_ptr()
+
+
+# ------------------------------------------------------------ pack / combine
+
+def pack_bf16(src, ring, chunk_bytes: int, chunk_begin: int, chunk_end: int, stream=None) -> None:
+    """src: F32 CUDA tensor (n elements); ring: 2-byte CUDA tensor."""
+    if src.element_size() != 4 or ring.element_size() != 2:
+        raise ValueError("src must be 4-byte, ring 2-byte elements")
+    _check(lib().xfer_pack_bf16(_dev(src), src.numel(), _dev(ring), ring.numel() * 2, chunk_bytes, chunk_begin,
+                                chunk_end, _stream(stream)), "xfer_pack_bf16")
+
+
+def pack_bf16_raw(src_ptr: int, n: int, ring_ptr: int, ring_bytes: int, chunk_bytes: int, chunk_begin: int,
+                  chunk_end: int, stream=None) -> int:
+    """Raw-pointer form; returns the status without raising."""
+    return lib().xfer_pack_bf16(src_ptr, n, ring_ptr, ring_bytes, chunk_bytes, chunk_begin, chunk_end,
+                                _stream(stream))
+
+
+def combine2(a, b, out, mode: int, stream=None) -> None:
+    """a, b: 2-byte CUDA tensors (BF16 patterns); out: F32 (mode 0) or 2-byte (mode 1)."""
+    n = a.numel()
+    if b.numel() != n or out.numel() != n:
+        raise ValueError("size mismatch")
+    if out.element_size() != (4 if mode == OUT_F32 else 2):
+        raise ValueError("output element size does not match the mode")
+    _check(lib().xfer_combine2(_dev(a), _dev(b), n, _dev(out), mode, _stream(stream)), "xfer_combine2")
+
+
+def combine2_raw(a_ptr: int, b_ptr: int, n: int, out_ptr: int, mode: int, stream=None) -> int:
+    return lib().xfer_combine2(a_ptr, b_ptr, n, out_ptr, mode, _stream(stream))
+
+
+# ------------------------------------------------------------------- argmax
+
+MAX_IDX = np.dtype([("max", "<f4"), ("idx", "<i4")])
+TOP2_REC = np.dtype([("top1", "<f4"), ("top2", "<f4"), ("idx", "<i4"), ("reserved", "<i4")])
+
+
+def argmax_workspace_bytes(rows: int, ncols0: int, ncols1: int) -> int:
+    return int(lib().xfer_argmax_workspace_bytes(rows, ncols0, ncols1))
+
+
+def shard(ptr: int, ld: int, rows: int, ncols: int, col_offset: int) -> Shard:
+    return Shard(ptr, ld, rows, ncols, col_offset)
+
+
+def argmax_merge(s0: Shard, s1: Shard, mode: int, out, workspace, stream=None) -> None:
+    """out: CUDA tensor of rows * 8 (ARGMAX) or rows * 16 (TOP2) bytes;
+    workspace: zero-filled CUDA tensor of argmax_workspace_bytes() bytes."""
+    _check(lib().xfer_argmax_merge(ctypes.byref(s0), ctypes.byref(s1), mode, _dev(out), _dev(workspace),
+                                   workspace.numel() * workspace.element_size(), _stream(stream)),
+           "xfer_argmax_merge")
+
+
+def argmax_merge_raw(s0: Shard, s1: Shard, mode: int, out_ptr: int, ws_ptr: int, ws_bytes: int,
+                     stream=None) -> int:
+    return lib().xfer_argmax_merge(ctypes.byref(s0), ctypes.byref(s1), mode, out_ptr, ws_ptr, ws_bytes,
+                                   _stream(stream))
+
+
+# --------------------------------------------------------------- run tables
+
+@dataclass
+class RunTable:
+    """Host arrays of a run-encoded table (lane-major)."""
+    runs_per_lane: np.ndarray   # uint32[n_lanes]
+    run_base: np.ndarray        # uint64[n_runs]
+    run_stride: np.ndarray      # int64[n_runs]
+    run_count: np.ndarray       # uint32[n_runs]
+    n_blocks: int
+    seg_bytes: int
+
+    @property
+    def n_lanes(self) -> int:
+        return int(self.runs_per_lane.size)
+
+    @property
+    def n_runs(self) -> int:
+        return int(self.run_base.size)
+
+    def c(self) -> RunTableC:
+        for name, dt in (("runs_per_lane", np.uint32), ("run_base", np.uint64), ("run_stride", np.int64),
+                         ("run_count", np.uint32)):
+            a = getattr(self, name)
+            if a.dtype != dt or not a.flags.c_contiguous:
+                setattr(self, name, np.ascontiguousarray(a, dtype=dt))
+        return RunTableC(self.n_lanes, self.n_blocks, self.seg_bytes, self.n_runs,
+                         self.runs_per_lane.ctypes.data, self.run_base.ctypes.data,
+                         self.run_stride.ctypes.data, self.run_count.ctypes.data)
+
+
+def runs_encode(addrs: np.ndarray, seg_bytes: int, max_count: int = 0) -> RunTable:
+    """Greedy run encoding of lane-major addresses [n_lanes, n_blocks]."""
+    a = np.ascontiguousarray(addrs, dtype=np.uint64)
+    n_lanes, n_blocks = a.shape
+    cap = max(1, n_lanes * n_blocks)
+    rpl = np.zeros(n_lanes, np.uint32)
+    base = np.zeros(cap, np.uint64)
+    stride = np.zeros(cap, np.int64)
+    count = np.zeros(cap, np.uint32)
+    nr = ctypes.c_uint64(0)
+    _check(lib().xfer_runs_encode(a.ctypes.data, n_lanes, n_blocks, max_count, rpl.ctypes.data, base.ctypes.data,
+                                  stride.ctypes.data, count.ctypes.data, cap, ctypes.byref(nr)), "xfer_runs_encode")
+    n = nr.value
+    return RunTable(rpl, base[:n].copy(), stride[:n].copy(), count[:n].copy(), n_blocks, seg_bytes)
+
+
+def _regions(regions):
+    arr = (Region * max(1, len(regions)))()
+    for i, (base, nbytes) in enumerate(regions):
+        arr[i] = Region(base, nbytes)
+    return arr
+
+
+def runs_validate_status(t: RunTable, regions, is_dst: bool) -> int:
+    tc = t.c()
+    return lib().xfer_runs_validate(ctypes.byref(tc), _regions(regions), len(regions), int(is_dst))
+
+
+def runs_plan_bytes(t: RunTable) -> int:
+    tc = t.c()
+    return int(lib().xfer_runs_plan_bytes(ctypes.byref(tc)))
+
+
+def runs_prepare_status(t: RunTable, regions, is_dst: bool, dev_ptr: int, dev_bytes: int):
+    tc = t.c()
+    plan = RunsPlan()
+    st = lib().xfer_runs_prepare(ctypes.byref(tc), _regions(regions), len(regions), int(is_dst), dev_ptr,
+                                 dev_bytes, ctypes.byref(plan))
+    return st, plan
+
+
+def runs_prepare(t: RunTable, regions, is_dst: bool, dev) -> RunsPlan:
+    """regions: list of (device base, bytes); dev: CUDA tensor holding the plan."""
+    st, plan = runs_prepare_status(t, regions, is_dst, _dev(dev), dev.numel() * dev.element_size())
+    _check(st, "xfer_runs_prepare")
+    return plan
+
+
+def gather_runs(plan: RunsPlan, staging, stream=None) -> None:
+    _check(lib().xfer_gather_runs(ctypes.byref(plan), _dev(staging), staging.numel() * staging.element_size(),
+                                  _stream(stream)), "xfer_gather_runs")
+
+
+def scatter_runs(staging, plan: RunsPlan, stream=None) -> None:
+    _check(lib().xfer_scatter_runs(_dev(staging), staging.numel() * staging.element_size(), ctypes.byref(plan),
+                                   _stream(stream)), "xfer_scatter_runs")
+
+
+def gather_runs_raw(plan: RunsPlan, staging_ptr: int, staging_bytes: int, stream=None) -> int:
+    return lib().xfer_gather_runs(ctypes.byref(plan), staging_ptr, staging_bytes, _stream(stream))
+
+
+def scatter_runs_raw(staging_ptr: int, staging_bytes: int, plan: RunsPlan, stream=None) -> int:
+    return lib().xfer_scatter_runs(staging_ptr, staging_bytes, ctypes.byref(plan), _stream(stream))

@@ -1,0 +1,254 @@
+// Two-shard argmax / top-2 merge over BF16 logit rows.
+//
+// Work split: every (row, shard) is cut into `splits` column slices and each
+// slice gets one workgroup, so even 16 rows keep hundreds of CUs busy (the
+// per-element key arithmetic would make a one-workgroup-per-row kernel
+// ALU-bound on 16 CUs).  Each workgroup reduces its slice to the slice's
+// first two elements and publishes them; the last workgroup of a row to
+// finish (an agent-scope counter in the workspace) folds the slices of each
+// shard, then the two shards, exactly as the exchange of per-shard records
+// is folded on the two-card drafter, and writes the row's record.
+//
+// Keys: inside a shard an element is the 32-bit key
+//     ord(value) << 16 | (0xFFFF - local column)
+// where ord maps BF16 bit patterns to 16-bit integers in numeric order with
+// -0 and +0 equal (0x8000 +- magnitude).  A larger key is earlier in the
+// row order (larger value, then lower id), keys are unique per shard, and 0
+// (below every finite value and -inf) marks "no element".  The first two
+// elements of any set follow from the pairwise merge
+//     top1 = max(x1, y1), top2 = max(min(x1, y1), max(x2, y2)).
+#include "internal.h"
+
+namespace xfer {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
+constexpr uint32_t kMaxSplits = 32;       // 2 * splits partials fit one wave
+constexpr uint32_t kTargetWorkgroups = 1024;
+constexpr uint32_t kMinSliceCols = 1024;
+
+__device__ __forceinline__ uint32_t ord16(uint32_t v) {
+  const uint32_t mag = v & 0x7FFFu;
+  return (v & 0x8000u) ? 0x8000u - mag : 0x8000u + mag;
+}
+
+__device__ __forceinline__ void take(uint32_t &t1, uint32_t &t2, uint32_t k) {
+  t2 = max(t2, min(t1, k));
+  t1 = max(t1, k);
+}
+
+__device__ __forceinline__ void merge(uint32_t &t1, uint32_t &t2, uint32_t o1, uint32_t o2) {
+  const uint32_t n2 = max(max(t2, o2), min(t1, o1));
+  t1 = max(t1, o1);
+  t2 = n2;
+}
+
+// One DPP step: lanes whose source is outside the pattern, or whose row is
+// masked off, read 0 (the identity of merge).
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ void dpp_merge(uint32_t &t1, uint32_t &t2) {
+  const uint32_t o1 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)t1, CTRL, ROW_MASK, 0xF, false);
+  const uint32_t o2 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)t2, CTRL, ROW_MASK, 0xF, false);
+  merge(t1, t2, o1, o2);
+}
+
+// Wavefront reduction; the full result ends in lane 63.
+__device__ __forceinline__ void wave_reduce(uint32_t &t1, uint32_t &t2) {
+  dpp_merge<0xB1, 0xF>(t1, t2);   // quad_perm [1,0,3,2]
+  dpp_merge<0x4E, 0xF>(t1, t2);   // quad_perm [2,3,0,1]: every lane holds its quad
+  dpp_merge<0x114, 0xF>(t1, t2);  // row_shr:4
+  dpp_merge<0x118, 0xF>(t1, t2);  // row_shr:8: lane 15 of each row holds the row
+  dpp_merge<0x142, 0xA>(t1, t2);  // row_bcast:15 into rows 1 and 3
+  dpp_merge<0x143, 0xC>(t1, t2);  // row_bcast:31 into rows 2 and 3: lane 63 holds all
+}
+
+struct Shards {
+  const uint16_t *ptr[2];
+  uint64_t ld[2];
+  uint32_t ncols[2];
+  uint32_t off[2];
+  uint32_t slice[2];  // columns per slice, a multiple of 8
+};
+
+template <int MODE>
+__global__ __launch_bounds__(kThreads) void argmax_kernel(Shards sh, uint32_t splits, void *out,
+                                                          uint64_t *partials, uint32_t *counters) {
+  const uint32_t per_row = 2 * splits;
+  const uint32_t row = blockIdx.x / per_row;
+  const uint32_t rem = blockIdx.x % per_row;
+  const uint32_t s = rem / splits;
+  const uint32_t k = rem % splits;
+  const uint32_t tid = threadIdx.x;
+
+  const uint32_t ncols = sh.ncols[s];
+  const uint32_t c0 = min(k * sh.slice[s], ncols);
+  const uint32_t c1 = min(c0 + sh.slice[s], ncols);
+  const uint16_t *rowp = sh.ptr[s] + (uint64_t)row * sh.ld[s];
+
+  uint32_t t1 = 0, t2 = 0;
+  // 16-byte vectors of 8 elements; c0 is a multiple of 8 and rows are 16-byte
+  // aligned, so every vector is aligned.
+  const uint32_t n_vec = (c1 - c0) / 8;
+  const uint4 *vp = reinterpret_cast<const uint4 *>(rowp + c0);
+  uint32_t v = tid;
+  for (; v + 3 * kThreads < n_vec; v += 4 * kThreads) {
+    uint4 w[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) w[u] = vp[v + u * kThreads];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint32_t id = 0xFFFFu - (c0 + 8 * (v + u * kThreads));
+      const uint32_t x[4] = {w[u].x, w[u].y, w[u].z, w[u].w};
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        take(t1, t2, (ord16(x[h] & 0xFFFFu) << 16) | (id - 2 * h));
+        take(t1, t2, (ord16(x[h] >> 16) << 16) | (id - 2 * h - 1));
+      }
+    }
+  }
+  for (; v < n_vec; v += kThreads) {
+    const uint4 w = vp[v];
+    const uint32_t id = 0xFFFFu - (c0 + 8 * v);
+    const uint32_t x[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      take(t1, t2, (ord16(x[h] & 0xFFFFu) << 16) | (id - 2 * h));
+      take(t1, t2, (ord16(x[h] >> 16) << 16) | (id - 2 * h - 1));
+    }
+  }
+  // Columns past the last whole vector (only in a shard's last slice).
+  const uint32_t c_tail = c0 + 8 * n_vec;
+  if (tid < c1 - c_tail) {
+    const uint32_t c = c_tail + tid;
+    take(t1, t2, (ord16(rowp[c]) << 16) | (0xFFFFu - c));
+  }
+
+  wave_reduce(t1, t2);
+  __shared__ uint32_t lds1[kWaves], lds2[kWaves];
+  __shared__ uint32_t last;
+  const uint32_t wave = tid / 64, lane = tid % 64;
+  if (lane == 63) {
+    lds1[wave] = t1;
+    lds2[wave] = t2;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    uint32_t a1 = lds1[0], a2 = lds2[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) merge(a1, a2, lds1[w], lds2[w]);
+    __hip_atomic_store(&partials[blockIdx.x], ((uint64_t)a1 << 32) | a2, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+    // Release our partial, then count; the workgroup that brings the count to
+    // per_row sees every other partial of the row.
+    const uint32_t prev =
+        __hip_atomic_fetch_add(&counters[row], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    last = (prev == per_row - 1);
+  }
+  __syncthreads();
+  if (!last || wave != 0) return;
+
+  // Fold (wave 0 of the row's last workgroup): lane i holds partial i; lanes
+  // [0, splits) are shard 0's slices, [splits, 2 * splits) shard 1's.
+  uint64_t p = 0;
+  if (lane < per_row)
+    p = __hip_atomic_load(&partials[(uint64_t)row * per_row + lane], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+  const bool in0 = lane < splits;
+  uint32_t a1 = in0 ? (uint32_t)(p >> 32) : 0, a2 = in0 ? (uint32_t)p : 0;
+  uint32_t b1 = in0 ? 0 : (uint32_t)(p >> 32), b2 = in0 ? 0 : (uint32_t)p;
+  wave_reduce(a1, a2);
+  wave_reduce(b1, b2);
+  if (lane != 63) return;
+
+  // Shard records -> global order (ord desc, global id asc).
+  struct Rec {
+    uint32_t ord;
+    uint32_t gid;
+    uint32_t shard;
+    uint32_t col;
+    bool has;
+  };
+  auto rec = [&](uint32_t key, uint32_t shard) {
+    Rec r;
+    r.has = key != 0;
+    r.ord = key >> 16;
+    r.col = 0xFFFFu - (key & 0xFFFFu);
+    r.gid = sh.off[shard] + r.col;
+    r.shard = shard;
+    return r;
+  };
+  auto before = [](const Rec &x, const Rec &y) {
+    if (!y.has) return x.has;
+    if (!x.has) return false;
+    if (x.ord != y.ord) return x.ord > y.ord;
+    return x.gid < y.gid;
+  };
+  const Rec x1 = rec(a1, 0), x2 = rec(a2, 0), y1 = rec(b1, 1), y2 = rec(b2, 1);
+  const bool x_wins = before(x1, y1);
+  const Rec &top1 = x_wins ? x1 : y1;
+  const Rec &lose1 = x_wins ? y1 : x1;
+  const Rec &win2 = x_wins ? x2 : y2;
+  const Rec &top2 = before(lose1, win2) ? lose1 : win2;
+  // Exact bits of the chosen elements (the key does not keep the sign of 0).
+  const uint32_t v1 = sh.ptr[top1.shard][(uint64_t)row * sh.ld[top1.shard] + top1.col];
+  if (MODE == XFER_ARGMAX) {
+    xfer_max_idx r;
+    r.max = __uint_as_float(v1 << 16);
+    r.idx = (int32_t)top1.gid;
+    reinterpret_cast<xfer_max_idx *>(out)[row] = r;
+  } else {
+    const uint32_t v2 = sh.ptr[top2.shard][(uint64_t)row * sh.ld[top2.shard] + top2.col];
+    xfer_top2 r;
+    r.top1 = __uint_as_float(v1 << 16);
+    r.top2 = __uint_as_float(v2 << 16);
+    r.idx = (int32_t)top1.gid;
+    r.reserved = 0;
+    reinterpret_cast<xfer_top2 *>(out)[row] = r;
+  }
+  // Leave the counter at zero for the next call on this workspace.
+  __hip_atomic_store(&counters[row], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+uint32_t round_up8(uint32_t x) { return (x + 7u) & ~7u; }
+
+}  // namespace
+
+uint32_t argmax_splits(uint32_t rows, uint32_t ncols0, uint32_t ncols1) {
+  if (rows == 0) return 1;
+  const uint32_t widest = ncols0 > ncols1 ? ncols0 : ncols1;
+  uint64_t want = (kTargetWorkgroups + 2ull * rows - 1) / (2ull * rows);
+  const uint64_t by_width = (widest + kMinSliceCols - 1) / kMinSliceCols;
+  if (want > by_width) want = by_width;
+  if (want > kMaxSplits) want = kMaxSplits;
+  if (want < 1) want = 1;
+  return (uint32_t)want;
+}
+
+// Layout: counters u32[rows] (padded to 16 bytes), then partials
+// u64[rows][2][splits].
+uint64_t argmax_workspace_bytes(uint32_t rows, uint32_t splits) {
+  const uint64_t counters = ((uint64_t)rows * 4 + 15) & ~15ull;
+  return counters + (uint64_t)rows * 2 * splits * 8;
+}
+
+hipError_t launch_argmax(ArgmaxShard s0, ArgmaxShard s1, uint32_t rows, int mode, void *out, void *workspace,
+                         uint32_t splits, hipStream_t stream) {
+  Shards sh;
+  const ArgmaxShard in[2] = {s0, s1};
+  for (int i = 0; i < 2; ++i) {
+    sh.ptr[i] = in[i].ptr;
+    sh.ld[i] = in[i].ld;
+    sh.ncols[i] = in[i].ncols;
+    sh.off[i] = in[i].col_offset;
+    sh.slice[i] = round_up8((in[i].ncols + splits - 1) / splits);
+  }
+  uint32_t *counters = reinterpret_cast<uint32_t *>(workspace);
+  uint64_t *partials = reinterpret_cast<uint64_t *>(reinterpret_cast<uint8_t *>(workspace) +
+                                                    (((uint64_t)rows * 4 + 15) & ~15ull));
+  const dim3 grid(rows * 2 * splits);
+  if (mode == XFER_ARGMAX)
+    return launch(argmax_kernel<XFER_ARGMAX>, grid, dim3(kThreads), 0, stream, sh, splits, out, partials, counters);
+  return launch(argmax_kernel<XFER_TOP2>, grid, dim3(kThreads), 0, stream, sh, splits, out, partials, counters);
+}
+
+}  // namespace xfer

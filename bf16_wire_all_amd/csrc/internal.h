@@ -1,0 +1,59 @@
+// Internal declarations shared by the host entry points and the kernel files
+// of libxfer.  Nothing here is exported.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "xfer.h"
+
+namespace xfer {
+
+// Launch a kernel through hipLaunchKernel so the launch status is returned
+// directly instead of being read back from the thread's sticky error slot.
+template <typename... KArgs, typename... Args>
+static inline hipError_t launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t lds, hipStream_t stream,
+                                Args... args) {
+  static_assert(sizeof...(KArgs) == sizeof...(Args), "argument count");
+  static_assert((std::is_same<KArgs, Args>::value && ...), "argument types must match the kernel exactly");
+  void *argv[] = {(void *)&args...};
+  return hipLaunchKernel((const void *)kernel, grid, block, argv, lds, stream);
+}
+
+// ---- pack / combine (pack_combine.hip)
+hipError_t launch_pack(const float *src, uint64_t n_elems, uint16_t *ring, uint64_t ring_elems,
+                       uint64_t slot0_elem, hipStream_t stream);
+hipError_t launch_combine(const uint16_t *a, const uint16_t *b, uint64_t n, void *out, int mode,
+                          hipStream_t stream);
+
+// ---- argmax (argmax.hip)
+struct ArgmaxShard {
+  const uint16_t *ptr;
+  uint64_t ld;
+  uint32_t ncols;
+  uint32_t col_offset;
+};
+uint32_t argmax_splits(uint32_t rows, uint32_t ncols0, uint32_t ncols1);
+uint64_t argmax_workspace_bytes(uint32_t rows, uint32_t splits);
+hipError_t launch_argmax(ArgmaxShard s0, ArgmaxShard s1, uint32_t rows, int mode, void *out, void *workspace,
+                         uint32_t splits, hipStream_t stream);
+
+// ---- run-table gather / scatter (runs_copy.hip)
+struct PlanView {
+  const uint32_t *tile_run;  // [n_lanes][n_tiles + 1]
+  const uint32_t *run_start; // [n_runs]
+  const uint64_t *run_base;  // [n_runs]
+  const int64_t *run_stride; // [n_runs]
+  uint32_t n_lanes, n_blocks, n_tiles, tile_blocks;
+  uint64_t seg_bytes;
+  uint32_t vps;       // 16-byte vectors per segment, <= kMaxSegVectors
+  uint32_t vps_log2;  // log2(vps) if vps is a power of two, else 32
+};
+constexpr uint32_t kMaxTileBlocks = 64;
+constexpr uint32_t kMaxSegVectors = 1u << 16;  // 1 MiB segments
+hipError_t launch_gather(const PlanView &p, void *staging, hipStream_t stream);
+hipError_t launch_scatter(const PlanView &p, const void *staging, hipStream_t stream);
+
+}  // namespace xfer

@@ -1,0 +1,166 @@
+// Pack (F32 -> BF16 into a slot ring) and two-operand combine kernels.
+//
+// Both are pure streams over HBM: 6 bytes per element for pack (4 read, 2
+// written), 8 (F32 out) or 6 (BF16 out) bytes per element for combine.  The
+// work per element is a handful of integer operations, far below the ALU
+// budget, so the design is about the memory side only:
+//   - a thread handles "quads" of 4 consecutive elements, so every load and
+//     store instruction of a wave covers one contiguous span (1 KiB of F32,
+//     512 B of BF16): fully coalesced 128-bit / 64-bit accesses;
+//   - each thread issues UNROLL independent loads before its first store, so
+//     enough bytes are in flight per CU to cover HBM latency;
+//   - a grid-stride loop over a grid sized to a few waves of workgroups per
+//     CU, so large inputs do not pay per-workgroup launch overhead.
+#include "internal.h"
+
+namespace xfer {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kUnroll = 4;
+constexpr uint32_t kMaxGrid = 256 * 8;  // 8 workgroups per CU on 256 CUs
+
+// Round-to-nearest-even of an F32 bit pattern to BF16 (in the low 16 bits).
+// Adding 0x7FFF plus the lowest kept bit carries into the kept bits exactly
+// when the discarded half is above one half, or equal to one half with an
+// odd kept part; overflow carries into the exponent and gives infinity.  NaN
+// patterns would be carried into infinity or zero, so they are replaced by
+// the canonical quiet NaN first.
+__device__ __forceinline__ uint32_t bf16_rne(uint32_t f) {
+  const uint32_t r = (f + 0x7FFFu + ((f >> 16) & 1u)) >> 16;
+  return ((f & 0x7FFFFFFFu) > 0x7F800000u) ? 0x7FC0u : r;
+}
+
+__device__ __forceinline__ uint2 pack_quad(uint4 v) {
+  uint2 o;
+  o.x = bf16_rne(v.x) | (bf16_rne(v.y) << 16);
+  o.y = bf16_rne(v.z) | (bf16_rne(v.w) << 16);
+  return o;
+}
+
+// F32 sum of two BF16 values given as the low / high half of a word pair,
+// with rank 0's operand first; NaN results canonical.
+__device__ __forceinline__ uint32_t sum_bf16(uint32_t a16, uint32_t b16) {
+  const float fa = __uint_as_float(a16 << 16);
+  const float fb = __uint_as_float(b16 << 16);
+  const uint32_t s = __float_as_uint(__fadd_rn(fa, fb));
+  return ((s & 0x7FFFFFFFu) > 0x7F800000u) ? 0x7FC00000u : s;
+}
+
+__device__ __forceinline__ uint4 sum_quad(uint2 a, uint2 b) {
+  uint4 s;
+  s.x = sum_bf16(a.x & 0xFFFFu, b.x & 0xFFFFu);
+  s.y = sum_bf16(a.x >> 16, b.x >> 16);
+  s.z = sum_bf16(a.y & 0xFFFFu, b.y & 0xFFFFu);
+  s.w = sum_bf16(a.y >> 16, b.y >> 16);
+  return s;
+}
+
+// src points at the first element of the call's range; quad q of the range
+// goes to ring quad (q + slot0_q) mod ring_q.  The range is at most one ring
+// long, so one conditional subtraction is the modulo.
+//
+// A range whose length is not a multiple of 4 ends in 1-3 single elements;
+// the first threads of workgroup 0 convert them.
+__global__ __launch_bounds__(kThreads) void pack_kernel(const uint4 *__restrict__ src, uint2 *__restrict__ ring,
+                                                        uint64_t n_quads, uint64_t ring_quads, uint64_t slot0_q,
+                                                        uint32_t tail) {
+  if (blockIdx.x == 0 && threadIdx.x < tail) {
+    const uint64_t ring_elems = ring_quads * 4;
+    uint64_t d = (n_quads + slot0_q) * 4 + threadIdx.x;
+    if (d >= ring_elems) d -= ring_elems;
+    const float *s1 = reinterpret_cast<const float *>(src + n_quads);
+    reinterpret_cast<uint16_t *>(ring)[d] = (uint16_t)bf16_rne(__float_as_uint(s1[threadIdx.x]));
+  }
+  const uint64_t stride = (uint64_t)gridDim.x * kThreads;
+  uint64_t q = (uint64_t)blockIdx.x * kThreads + threadIdx.x;
+  for (; q + (kUnroll - 1) * stride < n_quads; q += kUnroll * stride) {
+    uint4 v[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) v[u] = src[q + u * stride];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      uint64_t d = q + u * stride + slot0_q;
+      if (d >= ring_quads) d -= ring_quads;
+      ring[d] = pack_quad(v[u]);
+    }
+  }
+  for (; q < n_quads; q += stride) {
+    uint64_t d = q + slot0_q;
+    if (d >= ring_quads) d -= ring_quads;
+    ring[d] = pack_quad(src[q]);
+  }
+}
+
+// In BF16 mode out may be a or b itself: every thread reads its own quads
+// before writing them and no other thread touches them.
+template <int MODE>
+__global__ __launch_bounds__(kThreads) void combine_kernel(const uint2 *a, const uint2 *b, void *out,
+                                                           uint64_t n_quads, uint32_t tail) {
+  if (blockIdx.x == 0 && threadIdx.x < tail) {
+    const uint64_t e = n_quads * 4 + threadIdx.x;
+    const uint32_t s = sum_bf16(reinterpret_cast<const uint16_t *>(a)[e], reinterpret_cast<const uint16_t *>(b)[e]);
+    if (MODE == XFER_OUT_F32)
+      reinterpret_cast<uint32_t *>(out)[e] = s;
+    else
+      reinterpret_cast<uint16_t *>(out)[e] = (uint16_t)bf16_rne(s);
+  }
+  const uint64_t stride = (uint64_t)gridDim.x * kThreads;
+  uint64_t q = (uint64_t)blockIdx.x * kThreads + threadIdx.x;
+  for (; q + (kUnroll - 1) * stride < n_quads; q += kUnroll * stride) {
+    uint2 va[kUnroll], vb[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      va[u] = a[q + u * stride];
+      vb[u] = b[q + u * stride];
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const uint4 s = sum_quad(va[u], vb[u]);
+      if (MODE == XFER_OUT_F32) {
+        reinterpret_cast<uint4 *>(out)[q + u * stride] = s;
+      } else {
+        reinterpret_cast<uint2 *>(out)[q + u * stride] = pack_quad(s);
+      }
+    }
+  }
+  for (; q < n_quads; q += stride) {
+    const uint4 s = sum_quad(a[q], b[q]);
+    if (MODE == XFER_OUT_F32)
+      reinterpret_cast<uint4 *>(out)[q] = s;
+    else
+      reinterpret_cast<uint2 *>(out)[q] = pack_quad(s);
+  }
+}
+
+uint32_t grid_for(uint64_t n_quads) {
+  const uint64_t per_block = (uint64_t)kThreads * kUnroll;
+  uint64_t g = (n_quads + per_block - 1) / per_block;
+  if (g > kMaxGrid) g = kMaxGrid;
+  return (uint32_t)(g ? g : 1);
+}
+
+}  // namespace
+
+hipError_t launch_pack(const float *src, uint64_t n_elems, uint16_t *ring, uint64_t ring_elems,
+                       uint64_t slot0_elem, hipStream_t stream) {
+  const uint64_t n_quads = n_elems / 4;
+  const uint32_t tail = (uint32_t)(n_elems % 4);
+  return launch(pack_kernel, dim3(grid_for(n_quads)), dim3(kThreads), 0, stream,
+                reinterpret_cast<const uint4 *>(src), reinterpret_cast<uint2 *>(ring), n_quads, ring_elems / 4,
+                slot0_elem / 4, tail);
+}
+
+hipError_t launch_combine(const uint16_t *a, const uint16_t *b, uint64_t n, void *out, int mode,
+                          hipStream_t stream) {
+  const uint64_t n_quads = n / 4;
+  const uint32_t tail = (uint32_t)(n % 4);
+  const uint2 *a2 = reinterpret_cast<const uint2 *>(a);
+  const uint2 *b2 = reinterpret_cast<const uint2 *>(b);
+  const dim3 grid(grid_for(n_quads));
+  if (mode == XFER_OUT_F32)
+    return launch(combine_kernel<XFER_OUT_F32>, grid, dim3(kThreads), 0, stream, a2, b2, out, n_quads, tail);
+  return launch(combine_kernel<XFER_OUT_BF16>, grid, dim3(kThreads), 0, stream, a2, b2, out, n_quads, tail);
+}
+
+}  // namespace xfer

@@ -1,0 +1,307 @@
+/*
+ * xfer.h - C ABI of libxfer, the staging and combine kernels around a
+ * point-to-point tensor transfer, for AMD Instinct MI355X (gfx950).
+ *
+ * Pages the operations come from:
+ *   [CE]   llama.cpp PR "Large all-reduces under -sm tensor now go through the
+ *          copy engines" (Piggidragon fork, PR 16), section "Change".
+ *   [TP2]  "The two-card (TP = 2) DSpark worker" (TP2.md), sections "Layout"
+ *          and "Collectives".
+ *   [RUNS] pegaflow PR 350 "run-encode QueryBlocksForTransfer addresses and
+ *          coalesce RDMA READs", sections "Problem", "What this PR does" and
+ *          "Trust boundary".
+ *
+ * Conventions shared by every call:
+ *   - Pointers marked (device) are device addresses of the GPU that is current
+ *     on the calling thread; pointers marked (host) are host memory.  The
+ *     caller owns every buffer, including the run plans; the library keeps no
+ *     global state and allocates nothing.
+ *   - Hot calls (pack, combine, argmax, gather, scatter) only enqueue work on
+ *     `stream`: they never allocate, never synchronise and never block.
+ *     xfer_runs_prepare is the one blocking set-up call.
+ *   - Every call checks all its arguments on the host first.  On any status
+ *     other than XFER_OK nothing has been enqueued and no output byte has
+ *     been written; the outputs of a failed call must not be read.
+ *     XFER_E_DEVICE reports a launch the runtime refused.
+ *   - Empty work (n == 0, rows == 0, an empty chunk range, an empty table) is
+ *     XFER_OK with nothing enqueued.
+ *   - Every buffer a kernel streams through, and every row start and segment
+ *     address, must be 16-byte aligned: the kernels move 128-bit vectors.
+ *     Element counts may be anything.
+ *   - Results are deterministic and independent of launch shape: the same
+ *     inputs give the same bits on every call and on every GPU.
+ */
+#ifndef XFER_H
+#define XFER_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* The library is built with hidden visibility; only these calls are exported. */
+#define XFER_API __attribute__((visibility("default")))
+
+/* ------------------------------------------------------------ status codes */
+enum {
+  XFER_OK = 0,
+  XFER_E_INVAL = 1,       /* bad pointer, size, alignment, mode or aliasing   */
+  XFER_E_UNSUPPORTED = 2, /* valid request outside what the kernels handle    */
+  XFER_E_TABLE = 3,       /* run table inconsistent                           */
+  XFER_E_RANGE = 4,       /* a segment outside the declared regions, or an
+                             address computation that overflows 64 bits       */
+  XFER_E_OVERLAP = 5,     /* destination segments overlap each other          */
+  XFER_E_DEVICE = 6       /* the HIP runtime refused a launch or a copy       */
+};
+
+/* Static description of a status code (never NULL). */
+XFER_API const char *xfer_status_str(int status);
+
+/* -------------------------------------------------------------------- pack */
+
+/*
+ * xfer_pack_bf16 - [CE] "Change": a rank converts its F32 partial to BF16,
+ * round to nearest with ties to even, into fixed-size chunks of a staging
+ * ring; two slots alternate so one chunk can be converted while the previous
+ * one is in flight.
+ *
+ *   src          (device) F32[n], the rank's partial.
+ *   ring         (device) BF16 bit patterns, ring_bytes long, holding
+ *                R = ring_bytes / chunk_bytes slots of chunk_bytes each.
+ *   chunk_bytes  BF16 bytes per chunk (524288 = 512 KiB in [CE]); a multiple
+ *                of 16.  CE = chunk_bytes / 2 elements per chunk.
+ *   chunk_begin, chunk_end  the chunks this call packs.  Chunk c holds
+ *                elements [c*CE, min((c+1)*CE, n)) and is written to slot
+ *                c mod R: ring[(c mod R)*CE + j] = bf16_rne(src[c*CE + j]).
+ *                Ring bytes past a short last chunk are not written.
+ *
+ * Rounding: IEEE round-to-nearest-even on the bit pattern, subnormals
+ * rounded (not flushed), signs and infinities kept, every NaN written as the
+ * canonical quiet NaN 0x7FC0.
+ *
+ * Errors: XFER_E_INVAL if a pointer is NULL or not 16-byte aligned, if
+ * chunk_bytes is 0 or not a multiple of 16, if ring_bytes is not a non-zero
+ * multiple of chunk_bytes, if chunk_end - chunk_begin > R (two chunks of one
+ * call would share a slot), if a named chunk starts at or past n, or if src
+ * and ring overlap.
+ */
+XFER_API int xfer_pack_bf16(const float *src, size_t n, uint16_t *ring, size_t ring_bytes, size_t chunk_bytes,
+                   size_t chunk_begin, size_t chunk_end, hipStream_t stream);
+
+/* ----------------------------------------------------------------- combine */
+
+enum { XFER_OUT_F32 = 0, XFER_OUT_BF16 = 1 };
+
+/*
+ * xfer_combine2 - [CE] "Change" (the sum kernel) and [TP2] "Layout" (fp32
+ * sums rounded to bf16): out[i] = f32(a[i]) + f32(b[i]), one IEEE binary32
+ * addition with rank 0's value as the first operand on both ranks, so both
+ * ranks get identical bits.
+ *
+ *   a_rank0, b_rank1  (device) BF16 bit patterns, n each.
+ *   out               (device) F32[n] for XFER_OUT_F32, or BF16[n] for
+ *                     XFER_OUT_BF16 (the F32 sum rounded to nearest even).
+ *
+ * Subnormals are kept.  A NaN result is written as 0x7FC00000 (F32) or
+ * 0x7FC0 (BF16).
+ *
+ * Errors: XFER_E_INVAL for NULL or misaligned pointers, an unknown out_mode,
+ * or an output that overlaps an input (except out == a_rank0 or
+ * out == b_rank1 exactly in BF16 mode, which is computed in place).
+ */
+XFER_API int xfer_combine2(const uint16_t *a_rank0, const uint16_t *b_rank1, size_t n, void *out, int out_mode,
+                  hipStream_t stream);
+
+/* ------------------------------------------------------------ argmax merge */
+
+enum { XFER_ARGMAX = 0, XFER_TOP2 = 1 };
+
+/* One shard of a block of logit rows: BF16 bit patterns, row-major. */
+typedef struct {
+  const uint16_t *ptr; /* (device) element (0, 0) of the shard             */
+  size_t ld;           /* elements between the starts of consecutive rows  */
+  uint32_t rows;
+  uint32_t ncols;      /* 1 .. 65536                                       */
+  uint32_t col_offset; /* global id of the shard's column 0                */
+} xfer_shard;
+
+typedef struct {
+  float max;   /* exact F32 value of the winning BF16 element */
+  int32_t idx; /* its global id                               */
+} xfer_max_idx;  /* 8 bytes  */
+
+typedef struct {
+  float top1, top2; /* first and second element of the row's order    */
+  int32_t idx;      /* global id of top1                               */
+  int32_t reserved; /* written as 0                                    */
+} xfer_top2;        /* 16 bytes */
+
+/*
+ * xfer_argmax_merge - [TP2] "Layout": the vocabulary is split by columns
+ * between two ranks, rank 0 holding the lower ids so that a tie of the global
+ * argmax goes to the lower id as on one card; each rank's (shard max, index),
+ * or (top1, top2, index) when the margin is wanted, is exchanged and folded.
+ *
+ * Row order: larger value first (numeric, so -0 == +0), then the lower
+ * global id.  Per row, each shard's first two elements are found, then
+ * folded: global top1 is the earlier shard top1; global top2 is the earlier
+ * of the other shard's top1 and the winner's top2.  Values are the exact F32
+ * of the chosen BF16 elements (their own bits, so the sign of a zero is the
+ * chosen element's).  NaN logits are outside the contract: the output for a
+ * row holding a NaN is unspecified, but always a record of that row.
+ *
+ *   out        (device) xfer_max_idx[rows] (XFER_ARGMAX) or
+ *              xfer_top2[rows] (XFER_TOP2).
+ *   workspace  (device) at least xfer_argmax_workspace_bytes(rows, s0->ncols,
+ *              s1->ncols) bytes, 16-byte aligned, ZERO-FILLED before its first
+ *              use; every successful call leaves it zero-filled again.  Calls
+ *              that run concurrently must use different workspaces.
+ *
+ * Errors: XFER_E_INVAL for NULL or misaligned pointers (ptr and ld * 2 must
+ * be multiples of 16), different row counts, ncols == 0, shards whose id
+ * ranges overlap, col_offset + ncols > 2^31, an unknown mode, a small
+ * workspace, or an output overlapping the logits or the workspace;
+ * XFER_E_UNSUPPORTED for a shard wider than 65536 columns.
+ */
+XFER_API size_t xfer_argmax_workspace_bytes(uint32_t rows, uint32_t ncols0, uint32_t ncols1);
+XFER_API int xfer_argmax_merge(const xfer_shard *s0, const xfer_shard *s1, int mode, void *out, void *workspace,
+                      size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------- run tables */
+
+/*
+ * A run-encoded address table, [RUNS] "What this PR does": parallel arrays
+ * runs_per_lane / run_base / run_stride / run_count.  A lane is one slot's K
+ * or V segment across the blocks; along a lane the addresses of consecutive
+ * blocks form arithmetic runs addr = base + i * stride, i < count
+ * ([RUNS] "Problem").  Runs are stored lane after lane and cover the lane's
+ * blocks in order: run r of a lane covers blocks [start_r, start_r + count_r)
+ * with start_r the sum of the counts of the lane's earlier runs.
+ *
+ * All array pointers are (host).  run_base values are device addresses.
+ */
+typedef struct {
+  uint32_t n_lanes;
+  uint32_t n_blocks;
+  uint64_t seg_bytes; /* bytes per segment (4096 in [RUNS])            */
+  uint64_t n_runs;
+  const uint32_t *runs_per_lane; /* [n_lanes]                        */
+  const uint64_t *run_base;      /* [n_runs]                         */
+  const int64_t *run_stride;     /* [n_runs], ignored when count == 1 */
+  const uint32_t *run_count;     /* [n_runs]                         */
+} xfer_run_table;
+
+/* A device address range that segments may occupy. */
+typedef struct {
+  uint64_t base;
+  uint64_t bytes;
+} xfer_region;
+
+/*
+ * xfer_runs_encode - the holder side of [RUNS] "What this PR does": feed the
+ * segment addresses of each lane, block by block, into a greedy run
+ * accumulator.  A run holding one address takes the next non-zero delta
+ * (that fits a signed 64-bit stride) as its stride; a longer run grows while
+ * the delta equals its stride; any other address starts a new run.  The
+ * stride of a one-address run is written as 0.
+ *
+ *   addrs        (host) uint64[n_lanes][n_blocks], lane-major.
+ *   max_count    0 for unlimited, else the longest run allowed (1 gives one
+ *                run per segment, the unencoded worst case).
+ *   out arrays   (host) runs_per_lane[n_lanes]; run_base, run_stride and
+ *                run_count of capacity cap_runs each.
+ *   *n_runs_out  receives the number of runs written.
+ * Errors: XFER_E_INVAL for NULL pointers, XFER_E_RANGE if cap_runs is too
+ * small.  Host only; usable without a GPU.
+ */
+XFER_API int xfer_runs_encode(const uint64_t *addrs, uint32_t n_lanes, uint32_t n_blocks, uint32_t max_count,
+                     uint32_t *runs_per_lane, uint64_t *run_base, int64_t *run_stride, uint32_t *run_count,
+                     uint64_t cap_runs, uint64_t *n_runs_out);
+
+/*
+ * xfer_runs_validate - [RUNS] "Trust boundary": the table is remote input and
+ * is checked completely before any memory is touched.  Host only; usable
+ * without a GPU.  Checks, in this order, each failure returning at once:
+ *   XFER_E_INVAL  t or a needed array is NULL; n_regions < 0 or regions NULL
+ *                 with n_regions > 0; seg_bytes is 0 ("no zero-size slots")
+ *                 or not a multiple of 16; a region that wraps past 2^64;
+ *   XFER_E_UNSUPPORTED  n_runs or n_lanes * n_blocks above 2^32 - 1, or
+ *                 seg_bytes above 1 MiB;
+ *   XFER_E_TABLE  the runs_per_lane sum differs from n_runs, a run has count
+ *                 0, or a lane's counts do not sum to n_blocks;
+ *   XFER_E_RANGE  a run's base, or its stride when count > 1, is not a
+ *                 multiple of 16, or its address span [lowest address,
+ *                 highest address + seg_bytes) overflows 64 bits or does not
+ *                 lie inside one region;
+ *   XFER_E_OVERLAP (is_dst != 0 only) two segments share a byte: the
+ *                 result would depend on the order of the writes.
+ */
+XFER_API int xfer_runs_validate(const xfer_run_table *t, const xfer_region *regions, int n_regions, int is_dst);
+
+/*
+ * A validated table laid out for the kernels in a caller-owned device buffer.
+ * Caller-held plain data: copy it freely; it stays valid while `dev` holds
+ * what xfer_runs_prepare wrote there.  The remaining fields are private.
+ */
+typedef struct {
+  void *dev;          /* (device) the plan buffer                   */
+  uint64_t dev_bytes;
+  uint32_t n_lanes, n_blocks;
+  uint64_t seg_bytes;
+  uint64_t n_runs;
+  uint64_t span_lo, span_hi; /* byte range covering every segment      */
+  uint32_t is_dst;
+  uint32_t tile_blocks;      /* private from here on                   */
+  uint32_t n_tiles;
+  uint32_t magic;
+  uint64_t off_tile_run, off_run_start, off_run_base, off_run_stride;
+} xfer_runs_plan;
+
+/* Device bytes xfer_runs_prepare needs for table t (0 if t is NULL). */
+XFER_API size_t xfer_runs_plan_bytes(const xfer_run_table *t);
+
+/*
+ * xfer_runs_prepare - validate t exactly as xfer_runs_validate does, then
+ * write the kernels' form of it into dev (device, 16-byte aligned, at least
+ * xfer_runs_plan_bytes(t) bytes) with a blocking host-to-device copy, and
+ * fill *out.  Returns the validation status, XFER_E_INVAL for a small or
+ * misaligned dev, or XFER_E_DEVICE if the copy fails.
+ */
+XFER_API int xfer_runs_prepare(const xfer_run_table *t, const xfer_region *regions, int n_regions, int is_dst, void *dev,
+                      size_t dev_bytes, xfer_runs_plan *out);
+
+/*
+ * xfer_gather_runs - the data movement of [RUNS] "What this PR does" steps
+ * 2-4 (decode the runs and read every segment into a dense local buffer):
+ *   staging[(b * n_lanes + l) * seg_bytes + k] = *(addr(l, b) + k)
+ * for every lane l, block b and k < seg_bytes, with addr(l, b) decoded from
+ * the run of lane l that covers block b.  Staging is block-major, lanes
+ * inside a block.
+ *
+ *   staging  (device) at least n_lanes * n_blocks * seg_bytes bytes,
+ *            16-byte aligned, not overlapping [span_lo, span_hi).
+ * Errors: XFER_E_INVAL for a NULL / foreign / destination plan, a small,
+ * misaligned or overlapping staging buffer.
+ */
+XFER_API int xfer_gather_runs(const xfer_runs_plan *src_plan, void *staging, size_t staging_bytes, hipStream_t stream);
+
+/*
+ * xfer_scatter_runs - the inverse placement, [RUNS] "What this PR does" step
+ * 5 (every block placed at its own local address) done as data movement:
+ *   *(daddr(l, b) + k) = staging[(b * n_lanes + l) * seg_bytes + k]
+ * with daddr decoded from dst_plan (prepared with is_dst != 0, so its
+ * segments are disjoint).  No other destination byte is written.
+ * Errors: XFER_E_INVAL for a NULL / foreign / source plan, a small, misaligned
+ * or overlapping staging buffer.
+ */
+XFER_API int xfer_scatter_runs(const void *staging, size_t staging_bytes, const xfer_runs_plan *dst_plan,
+                      hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* XFER_H */
