@@ -1,0 +1,297 @@
+#!/usr/bin/env python3
+"""Benchmark of the transfer staging / combine hot path on one MI355X.
+
+One step is one pass of every hot-path kernel over one batch of synthetic,
+HBM-resident input:
+  pack_bf16 rank 0, pack_bf16 rank 1   2048 x 5120 F32 partials -> BF16, 512 KiB
+                                       chunks (bulk: every chunk in one call)
+  gather_runs                          1000 blocks x 288 slots x 2 x 4 KiB from two
+                                       bump-allocated regions -> dense staging
+  scatter_runs                         staging -> destination, 12 KiB slot stride
+  argmax_merge (top1, top2, idx)       16 rows x 129280 BF16 logits, 2 shards
+  combine2 (F32 out)                   the two packed partials summed in F32
+combine runs last so its inputs, written by the packs, have been pushed out
+of the caches by the 9.4 GB the gather and scatter stream: every kernel
+reads from HBM, as in a cold pipeline.
+
+Prints ONE JSON line: value = algorithmic bytes of the whole step / wall
+time of the step (GB/s, decimal).  Per-kernel durations come from HIP events
+recorded on the stream the kernels are launched on, over the timed region.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0            # MI355X HBM3E, published
+CHUNK = 512 * 1024               # BF16 bytes per chunk
+TOKENS, HIDDEN = 2048, 5120
+ROWS, VOCAB, SPLIT = 16, 129280, 64768
+N_BLOCKS, N_SLOTS, SEG, DST_SLOT_STRIDE = 1000, 288, 4096, 12288
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes():
+    n = TOKENS * HIDDEN
+    kv = N_BLOCKS * N_SLOTS * 2 * SEG
+    return {
+        "pack_rank0": 6 * n,                 # 4 B read + 2 B written per element
+        "pack_rank1": 6 * n,
+        "gather": 2 * kv,                    # every segment read once and written once
+        "scatter": 2 * kv,
+        "argmax_top2": ROWS * VOCAB * 2 + ROWS * 16,
+        "combine_f32": 8 * n,                # 2 + 2 B read, 4 B written per element
+    }
+
+
+def source_hash(name):
+    with open(os.path.join(ROOT, "bf16_wire_all_amd", "csrc", name), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(kernel_file, key):
+    """HBM bytes per launch from the committed rocprofv3 PMC summary, if it
+    was taken on the kernel source as it is now (else None)."""
+    path = os.path.join(ROOT, "profiles", "pmc_traffic.json")
+    try:
+        with open(path) as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        return None
+    entry = data.get(key)
+    if not entry or entry.get("source_sha256_16") != source_hash(kernel_file):
+        return None
+    return entry.get("traffic_bytes_per_launch")
+
+
+class Workload:
+    """Device buffers of one step, filled from the seeded generators."""
+
+    def __init__(self, dev):
+        import numpy as np
+        import torch
+
+        import bf16_wire_all_amd as x
+        import datagen as dg
+
+        self.x, self.torch, self.np = x, torch, np
+        n = TOKENS * HIDDEN
+        self.n = n
+        self.n_chunks = -(-n // (CHUNK // 2))
+        log("bench: generating inputs")
+        self.a_host = dg.prompt_partial(n, dg.seed_for(2, 0, TOKENS))
+        self.b_host = dg.prompt_partial(n, dg.seed_for(2, 1, TOKENS))
+        self.a = torch.from_numpy(self.a_host).to(dev)
+        self.b = torch.from_numpy(self.b_host).to(dev)
+        # BF16 bit patterns are held in int16 tensors (2-byte elements)
+        self.ring_a = torch.zeros(self.n_chunks * CHUNK // 2, dtype=torch.int16, device=dev)
+        self.ring_b = torch.zeros(self.n_chunks * CHUNK // 2, dtype=torch.int16, device=dev)
+        self.sum = torch.zeros(n, dtype=torch.float32, device=dev)
+
+        inp = dg.argmax_logits(ROWS, dg.seed_for(3))
+        self.logits_host = inp.logits
+        self.logits = torch.from_numpy(inp.logits.view(np.int16).copy()).to(dev)
+        p = self.logits.data_ptr()
+        self.s0 = x.shard(p, VOCAB, ROWS, SPLIT, 0)
+        self.s1 = x.shard(p + 2 * SPLIT, VOCAB, ROWS, VOCAB - SPLIT, SPLIT)
+        self.ws = torch.zeros(x.argmax_workspace_bytes(ROWS, SPLIT, VOCAB - SPLIT), dtype=torch.uint8, device=dev)
+        self.top2 = torch.zeros(ROWS * 16, dtype=torch.uint8, device=dev)
+
+        rb = dg.region_bytes_for(N_BLOCKS, N_SLOTS, SEG)
+        self.regions = [torch.empty(rb, dtype=torch.uint8, device=dev) for _ in range(2)]
+        bases = [r.data_ptr() for r in self.regions]
+        self.src_addrs = dg.kv_src_addrs(N_BLOCKS, N_SLOTS, SEG, bases)
+        self.region_hosts = []
+        for i, r in enumerate(self.regions):
+            h = np.empty(rb, np.uint8)
+            dg.fill_region(h, bases[i], self.src_addrs, SEG, dg.seed_for(4, 0, i))
+            r.copy_(torch.from_numpy(h))
+            self.region_hosts.append(h)
+        self.src_table = x.runs_encode(self.src_addrs, SEG)
+        self.src_plan_buf = torch.zeros(x.runs_plan_bytes(self.src_table), dtype=torch.uint8, device=dev)
+        self.src_plan = x.runs_prepare(self.src_table, [(b, rb) for b in bases], False, self.src_plan_buf)
+        self.staging = torch.empty(2 * N_SLOTS * N_BLOCKS * SEG, dtype=torch.uint8, device=dev)
+        self.dst = torch.full((N_BLOCKS * N_SLOTS * DST_SLOT_STRIDE,), 0xA5, dtype=torch.uint8, device=dev)
+        self.dst_addrs = dg.kv_dst_addrs(N_BLOCKS, N_SLOTS, SEG, self.dst.data_ptr(), DST_SLOT_STRIDE)
+        self.dst_table = x.runs_encode(self.dst_addrs, SEG)
+        self.dst_plan_buf = torch.zeros(x.runs_plan_bytes(self.dst_table), dtype=torch.uint8, device=dev)
+        self.dst_plan = x.runs_prepare(self.dst_table, [(self.dst.data_ptr(), self.dst.numel())], True,
+                                       self.dst_plan_buf)
+        torch.cuda.synchronize()
+
+    def kernels(self):
+        """(name, callable) in step order; each callable enqueues one call."""
+        x = self.x
+        n, nc = self.n, self.n_chunks
+        ra, rb = self.ring_a, self.ring_b
+        return [
+            ("pack_rank0", lambda: x.pack_bf16(self.a, ra, CHUNK, 0, nc)),
+            ("pack_rank1", lambda: x.pack_bf16(self.b, rb, CHUNK, 0, nc)),
+            ("gather", lambda: x.gather_runs(self.src_plan, self.staging)),
+            ("scatter", lambda: x.scatter_runs(self.staging, self.dst_plan)),
+            ("argmax_top2", lambda: x.argmax_merge(self.s0, self.s1, x.TOP2, self.top2, self.ws)),
+            ("combine_f32", lambda: x.combine2(ra[:n], rb[:n], self.sum, x.OUT_F32)),
+        ]
+
+
+def run_gpu(steps, warmup):
+    import torch
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = Workload(dev)
+    ks = w.kernels()
+    log(f"bench: warmup {warmup} steps")
+    for _ in range(warmup):
+        for _, k in ks:
+            k()
+    torch.cuda.synchronize()
+    events = {name: [] for name, _ in ks}
+    log(f"bench: timing {steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        for name, k in ks:
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            k()
+            e1.record()
+            events[name].append((e0, e1))
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    per_kernel_ms = {name: sum(a.elapsed_time(b) for a, b in ev) / len(ev) for name, ev in events.items()}
+    return w, elapsed, per_kernel_ms
+
+
+def cpu_baseline(w, budget_s=12.0):
+    """The oracle, as it is, on this host: the same step (same sizes, same
+    inputs) repeated until about budget_s seconds of work; buffers are
+    allocated and touched before the clock starts."""
+    import numpy as np
+
+    import oracle
+
+    n = w.n
+    ce = CHUNK // 2
+    ring_a = np.ones(w.n_chunks * ce, np.uint16)
+    ring_b = np.ones(w.n_chunks * ce, np.uint16)
+    regions = [(r.data_ptr(), h) for r, h in zip(w.regions, w.region_hosts)]
+    src_t = oracle.RunTable(w.src_table.runs_per_lane, w.src_table.run_base, w.src_table.run_stride,
+                            w.src_table.run_count, N_BLOCKS)
+    dst_t = oracle.RunTable(w.dst_table.runs_per_lane, w.dst_table.run_base, w.dst_table.run_stride,
+                            w.dst_table.run_count, N_BLOCKS)
+    staging = np.ones(2 * N_SLOTS * N_BLOCKS * SEG, np.uint8)
+    dst = np.full(N_BLOCKS * N_SLOTS * DST_SLOT_STRIDE, 0xA5, np.uint8)
+    dst_regions = [(w.dst.data_ptr(), dst)]
+    step_bytes = sum(algorithmic_bytes().values())
+    reps, t_total = 0, 0.0
+    while t_total < budget_s and reps < 50:
+        t0 = time.perf_counter()
+        oracle.pack(w.a_host, ring_a.size, ce, 0, w.n_chunks, ring=ring_a)
+        oracle.pack(w.b_host, ring_b.size, ce, 0, w.n_chunks, ring=ring_b)
+        oracle.gather(src_t, SEG, regions, staging=staging)
+        oracle.scatter(dst_t, SEG, dst_regions, staging)
+        oracle.argmax_merge(w.logits_host, SPLIT, 1)
+        oracle.combine2(ring_a[:n], ring_b[:n], 0)
+        t_total += time.perf_counter() - t0
+        reps += 1
+    return {
+        "value": round(step_bytes * reps / t_total / 1e9, 3),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"{reps} full steps of the same workload (same sizes and inputs), single-threaded C oracle, "
+                  f"{t_total:.1f} s; host has {os.cpu_count()} logical CPUs",
+    }
+
+
+def calib_copy(gib=1, reps=5):
+    """A plain device copy of known size, for scaling rocprofv3 FETCH_SIZE /
+    WRITE_SIZE readings to bytes."""
+    import torch
+
+    n = gib << 30
+    a = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+    b = torch.empty_like(a)
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    log(f"calib: {reps} copies of {n} bytes")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy", action="store_true", help="run only the copy used to scale PMC readings")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}): the hot path here is single-GPU "
+              "by design; see the sharding notes in DESIGN.md", file=sys.stderr)
+        sys.exit(2)
+    if args.calib_copy:
+        calib_copy()
+        return
+    if args.steps < 1:
+        sys.exit("--steps must be >= 1")
+
+    w, elapsed, kms = run_gpu(args.steps, args.warmup)
+    ab = algorithmic_bytes()
+    step_bytes = sum(ab.values())
+    ms_per_step = elapsed / args.steps * 1e3
+    value = step_bytes * args.steps / elapsed / 1e9
+    kernels = {}
+    for name, ms in kms.items():
+        gbs = ab[name] / (ms * 1e-3) / 1e9
+        kernels[name] = {"us": round(ms * 1e3, 2), "bytes": ab[name], "GBps": round(gbs, 1),
+                         "frac_of_peak": round(gbs / PEAK_HBM_GBS, 4)}
+    g_gbs = ab["gather"] / (kms["gather"] * 1e-3) / 1e9
+    roofline = {"kernel": "gather_runs (paged K/V, 576 runs)", "bound": "hbm", "achieved": round(g_gbs, 1),
+                "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(g_gbs / PEAK_HBM_GBS, 4),
+                "traffic": measured_traffic("runs_copy.hip", "gather_dense")}
+    line = {
+        "metric": "achieved HBM GB/s (and % of peak) for pack+combine and run-table segment gather",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32+bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "transfer hot path: pack x2 + combine2 (2048x5120 F32 partials, 512 KiB BF16 chunks), "
+                        "argmax merge (16x129280 BF16, split at 64768, top2), gather+scatter by run table "
+                        "(1000 blocks x 288 slots x 2 x 4 KiB, one run per lane)",
+            "step_bytes": step_bytes,
+            "parallelism": "single GPU; both ranks emulated in one HBM",
+        },
+        "kernels": kernels,
+        "pack_combine_GBps": round((ab["pack_rank0"] + ab["pack_rank1"] + ab["combine_f32"]) /
+                                   ((kms["pack_rank0"] + kms["pack_rank1"] + kms["combine_f32"]) * 1e-3) / 1e9, 1),
+        "roofline": roofline,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("bench: cpu baseline (oracle)")
+        line["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

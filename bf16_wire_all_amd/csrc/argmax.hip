@@ -150,9 +150,14 @@ __global__ __launch_bounds__(kThreads) void argmax_kernel(Shards sh, uint32_t sp
 
   // Fold (wave 0 of the row's last workgroup): lane i holds partial i; lanes
   // [0, splits) are shard 0's slices, [splits, 2 * splits) shard 1's.
+  // Every workgroup of the row has published, so nothing else touches these
+  // partials in this call: read them, then clear them for the next call.
   uint64_t p = 0;
-  if (lane < per_row)
-    p = __hip_atomic_load(&partials[(uint64_t)row * per_row + lane], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+  if (lane < per_row) {
+    uint64_t *slot = &partials[(uint64_t)row * per_row + lane];
+    p = __hip_atomic_load(slot, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(slot, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
   const bool in0 = lane < splits;
   uint32_t a1 = in0 ? (uint32_t)(p >> 32) : 0, a2 = in0 ? (uint32_t)p : 0;
   uint32_t b1 = in0 ? 0 : (uint32_t)(p >> 32), b2 = in0 ? 0 : (uint32_t)p;
