@@ -55,8 +55,9 @@ class RunsPlan(ctypes.Structure):
     _fields_ = [("dev", ctypes.c_void_p), ("dev_bytes", ctypes.c_uint64), ("n_lanes", ctypes.c_uint32),
                 ("n_blocks", ctypes.c_uint32), ("seg_bytes", ctypes.c_uint64), ("n_runs", ctypes.c_uint64),
                 ("span_lo", ctypes.c_uint64), ("span_hi", ctypes.c_uint64), ("is_dst", ctypes.c_uint32),
-                ("tile_blocks", ctypes.c_uint32), ("n_tiles", ctypes.c_uint32), ("magic", ctypes.c_uint32),
-                ("off_tile_run", ctypes.c_uint64), ("off_run_start", ctypes.c_uint64),
+                ("tile_blocks", ctypes.c_uint32), ("n_tiles", ctypes.c_uint32), ("group_blocks", ctypes.c_uint32),
+                ("n_groups", ctypes.c_uint32), ("magic", ctypes.c_uint32),
+                ("off_group_run", ctypes.c_uint64), ("off_run_start", ctypes.c_uint64),
                 ("off_run_base", ctypes.c_uint64), ("off_run_stride", ctypes.c_uint64)]
 
 
@@ -170,7 +171,8 @@ def shard(ptr: int, ld: int, rows: int, ncols: int, col_offset: int) -> Shard:
 
 def argmax_merge(s0: Shard, s1: Shard, mode: int, out, workspace, stream=None) -> None:
     """out: CUDA tensor of rows * 8 (ARGMAX) or rows * 16 (TOP2) bytes;
-    workspace: zero-filled CUDA tensor of argmax_workspace_bytes() bytes."""
+    workspace: CUDA tensor of at least argmax_workspace_bytes() bytes, any
+    contents (the call fills and reads it)."""
     _check(lib().xfer_argmax_merge(ctypes.byref(s0), ctypes.byref(s1), mode, _dev(out), _dev(workspace),
                                    workspace.numel() * workspace.element_size(), _stream(stream)),
            "xfer_argmax_merge")

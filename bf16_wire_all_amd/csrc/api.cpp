@@ -14,7 +14,8 @@ namespace {
 using xfer::PlanView;
 
 constexpr uint32_t kPlanMagic = 0x584E5552u;  // "RUNX"
-constexpr uint32_t kDefaultTileBlocks = 32;
+constexpr uint32_t kDefaultTileBlocks = 2;    // blocks per gather/scatter workgroup
+constexpr uint32_t kDefaultGroupBlocks = 32;  // blocks per run-index entry
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -42,25 +43,22 @@ bool run_addr(uint64_t base, int64_t stride, uint64_t k, uint64_t *out) {
   return true;
 }
 
-uint32_t tile_blocks_for(uint32_t n_blocks) {
-  if (n_blocks == 0) return 1;
-  return n_blocks < kDefaultTileBlocks ? n_blocks : kDefaultTileBlocks;
-}
-
 // Byte layout of a plan inside its device buffer.
 struct Layout {
-  uint32_t tile_blocks, n_tiles;
-  uint64_t off_tile_run, off_run_start, off_run_base, off_run_stride, total;
+  uint32_t tile_blocks, n_tiles, group_blocks, n_groups;
+  uint64_t off_group_run, off_run_start, off_run_base, off_run_stride, total;
 };
 
 uint64_t up16(uint64_t x) { return (x + 15u) & ~15ull; }
 
 Layout layout_for(const xfer_run_table *t) {
   Layout L{};
-  L.tile_blocks = tile_blocks_for(t->n_blocks);
-  L.n_tiles = t->n_blocks ? (t->n_blocks + L.tile_blocks - 1) / L.tile_blocks : 0;
-  L.off_tile_run = 0;
-  L.off_run_start = up16((uint64_t)t->n_lanes * (L.n_tiles + 1) * 4);
+  L.tile_blocks = kDefaultTileBlocks;
+  L.group_blocks = kDefaultGroupBlocks;
+  L.n_tiles = (t->n_blocks + L.tile_blocks - 1) / L.tile_blocks;
+  L.n_groups = (t->n_blocks + L.group_blocks - 1) / L.group_blocks;
+  L.off_group_run = 0;
+  L.off_run_start = up16((uint64_t)t->n_lanes * (L.n_groups + 1) * 4);
   L.off_run_base = L.off_run_start + up16(t->n_runs * 4);
   L.off_run_stride = L.off_run_base + up16(t->n_runs * 8);
   L.total = L.off_run_stride + up16(t->n_runs * 8);
@@ -141,6 +139,8 @@ int validate(const xfer_run_table *t, const xfer_region *regions, int n_regions,
 bool plan_ok(const xfer_runs_plan *p) {
   if (!p || p->magic != kPlanMagic || !p->dev) return false;
   if (p->tile_blocks == 0 || p->tile_blocks > xfer::kMaxTileBlocks) return false;
+  if (p->group_blocks == 0 || p->group_blocks > xfer::kMaxGroupBlocks || p->group_blocks % p->tile_blocks)
+    return false;
   if (p->off_run_stride + up16(p->n_runs * 8) > p->dev_bytes) return false;
   return true;
 }
@@ -148,7 +148,7 @@ bool plan_ok(const xfer_runs_plan *p) {
 PlanView view_of(const xfer_runs_plan *p) {
   const uint8_t *d = reinterpret_cast<const uint8_t *>(p->dev);
   PlanView v;
-  v.tile_run = reinterpret_cast<const uint32_t *>(d + p->off_tile_run);
+  v.group_run = reinterpret_cast<const uint32_t *>(d + p->off_group_run);
   v.run_start = reinterpret_cast<const uint32_t *>(d + p->off_run_start);
   v.run_base = reinterpret_cast<const uint64_t *>(d + p->off_run_base);
   v.run_stride = reinterpret_cast<const int64_t *>(d + p->off_run_stride);
@@ -156,6 +156,8 @@ PlanView view_of(const xfer_runs_plan *p) {
   v.n_blocks = p->n_blocks;
   v.n_tiles = p->n_tiles;
   v.tile_blocks = p->tile_blocks;
+  v.group_blocks = p->group_blocks;
+  v.n_groups = p->n_groups;
   v.seg_bytes = p->seg_bytes;
   v.vps = (uint32_t)(p->seg_bytes / 16);
   v.vps_log2 = 32;
@@ -345,23 +347,24 @@ int xfer_runs_prepare(const xfer_run_table *t, const xfer_region *regions, int n
   const Layout L = layout_for(t);
   if (L.total && (!dev || !aligned16(dev) || dev_bytes < L.total)) return XFER_E_INVAL;
 
-  // Host image of the plan: per (lane, tile) the run covering the tile's
-  // first block, then each lane's end; per run its first block within its lane.
+  // Host image of the plan: per (lane, group of blocks) the run covering the
+  // group's first block, then each lane's end; per run its first block
+  // within its lane.
   std::vector<uint8_t> img(L.total, 0);
-  uint32_t *tile_run = reinterpret_cast<uint32_t *>(img.data() + L.off_tile_run);
+  uint32_t *group_run = reinterpret_cast<uint32_t *>(img.data() + L.off_group_run);
   uint32_t *run_start = reinterpret_cast<uint32_t *>(img.data() + L.off_run_start);
   uint64_t r = 0;
   for (uint32_t l = 0; l < t->n_lanes; ++l) {
-    uint32_t *tr = tile_run + (uint64_t)l * (L.n_tiles + 1);
-    uint32_t start = 0, tile = 0;
+    uint32_t *gr = group_run + (uint64_t)l * (L.n_groups + 1);
+    uint32_t start = 0, group = 0;
     for (uint32_t k = 0; k < t->runs_per_lane[l]; ++k, ++r) {
       run_start[r] = start;
       const uint32_t end = start + t->run_count[r];
-      // every tile whose first block lies in [start, end) starts in run r
-      while (tile < L.n_tiles && tile * L.tile_blocks < end) tr[tile++] = (uint32_t)r;
+      // every group whose first block lies in [start, end) starts in run r
+      while (group < L.n_groups && (uint64_t)group * L.group_blocks < end) gr[group++] = (uint32_t)r;
       start = end;
     }
-    tr[L.n_tiles] = (uint32_t)r;
+    gr[L.n_groups] = (uint32_t)r;
   }
   if (t->n_runs) {
     std::memcpy(img.data() + L.off_run_base, t->run_base, t->n_runs * 8);
@@ -383,8 +386,10 @@ int xfer_runs_prepare(const xfer_run_table *t, const xfer_region *regions, int n
   p.is_dst = is_dst ? 1u : 0u;
   p.tile_blocks = L.tile_blocks;
   p.n_tiles = L.n_tiles;
+  p.group_blocks = L.group_blocks;
+  p.n_groups = L.n_groups;
   p.magic = kPlanMagic;
-  p.off_tile_run = L.off_tile_run;
+  p.off_group_run = L.off_group_run;
   p.off_run_start = L.off_run_start;
   p.off_run_base = L.off_run_base;
   p.off_run_stride = L.off_run_stride;

@@ -1,13 +1,20 @@
 // Two-shard argmax / top-2 merge over BF16 logit rows.
 //
-// Work split: every (row, shard) is cut into `splits` column slices and each
-// slice gets one workgroup, so even 16 rows keep hundreds of CUs busy (the
-// per-element key arithmetic would make a one-workgroup-per-row kernel
-// ALU-bound on 16 CUs).  Each workgroup reduces its slice to the slice's
-// first two elements and publishes them; the last workgroup of a row to
-// finish (an agent-scope counter in the workspace) folds the slices of each
-// shard, then the two shards, exactly as the exchange of per-shard records
-// is folded on the two-card drafter, and writes the row's record.
+// Two launches on the caller's stream:
+//   1. scan: every (row, shard) is cut into `splits` column slices and each
+//      slice gets one workgroup, so even 16 rows keep hundreds of CUs busy
+//      (the per-element key arithmetic would make a one-workgroup-per-row
+//      kernel ALU-bound on 16 CUs).  Each workgroup reduces its slice to the
+//      slice's first two elements and writes them to the workspace.
+//   2. fold: one wavefront per row folds the slices of each shard into the
+//      shard's record, then the two shard records exactly as the exchange of
+//      (top1, top2, index) records is folded on the two-card drafter, and
+//      writes the row's output.
+// The kernel boundary orders the two steps, so no atomics or device-scope
+// fences are needed.  (A single kernel whose last workgroup per row folds,
+// found through a per-row atomic counter, measured 2-3x slower on MI355X:
+// the counter updates of a row's workgroups serialise, and an agent-scope
+// release in every workgroup writes back L2.)
 //
 // Keys: inside a shard an element is the 32-bit key
 //     ord(value) << 16 | (0xFFFF - local column)
@@ -17,6 +24,7 @@
 // (below every finite value and -inf) marks "no element".  The first two
 // elements of any set follow from the pairwise merge
 //     top1 = max(x1, y1), top2 = max(min(x1, y1), max(x2, y2)).
+// The wavefront reductions use DPP lane moves.
 #include "internal.h"
 
 namespace xfer {
@@ -24,9 +32,11 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
-constexpr uint32_t kMaxSplits = 32;       // 2 * splits partials fit one wave
+constexpr uint32_t kMaxSplits = 32;  // 2 * splits partials fit one wavefront
 constexpr uint32_t kTargetWorkgroups = 1024;
 constexpr uint32_t kMinSliceCols = 1024;
+
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ uint32_t ord16(uint32_t v) {
   const uint32_t mag = v & 0x7FFFu;
@@ -42,6 +52,17 @@ __device__ __forceinline__ void merge(uint32_t &t1, uint32_t &t2, uint32_t o1, u
   const uint32_t n2 = max(max(t2, o2), min(t1, o1));
   t1 = max(t1, o1);
   t2 = n2;
+}
+
+// The 8 elements of a 16-byte vector whose first column is `col`.
+__device__ __forceinline__ void take8(uint32_t &t1, uint32_t &t2, v4u w, uint32_t col) {
+  const uint32_t id = 0xFFFFu - col;
+  const uint32_t x[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    take(t1, t2, (ord16(x[h] & 0xFFFFu) << 16) | (id - 2 * h));
+    take(t1, t2, (ord16(x[h] >> 16) << 16) | (id - 2 * h - 1));
+  }
 }
 
 // One DPP step: lanes whose source is outside the pattern, or whose row is
@@ -71,9 +92,8 @@ struct Shards {
   uint32_t slice[2];  // columns per slice, a multiple of 8
 };
 
-template <int MODE>
-__global__ __launch_bounds__(kThreads) void argmax_kernel(Shards sh, uint32_t splits, void *out,
-                                                          uint64_t *partials, uint32_t *counters) {
+// Workgroup (row, shard s, slice k) -> partials[blockIdx.x] = (top1 << 32 | top2).
+__global__ __launch_bounds__(kThreads) void argmax_scan_kernel(Shards sh, uint32_t splits, uint64_t *partials) {
   const uint32_t per_row = 2 * splits;
   const uint32_t row = blockIdx.x / per_row;
   const uint32_t rem = blockIdx.x % per_row;
@@ -90,33 +110,15 @@ __global__ __launch_bounds__(kThreads) void argmax_kernel(Shards sh, uint32_t sp
   // 16-byte vectors of 8 elements; c0 is a multiple of 8 and rows are 16-byte
   // aligned, so every vector is aligned.
   const uint32_t n_vec = (c1 - c0) / 8;
-  const uint4 *vp = reinterpret_cast<const uint4 *>(rowp + c0);
+  const v4u *vp = reinterpret_cast<const v4u *>(rowp + c0);
   uint32_t v = tid;
-  for (; v + 3 * kThreads < n_vec; v += 4 * kThreads) {
-    uint4 w[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) w[u] = vp[v + u * kThreads];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const uint32_t id = 0xFFFFu - (c0 + 8 * (v + u * kThreads));
-      const uint32_t x[4] = {w[u].x, w[u].y, w[u].z, w[u].w};
-#pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        take(t1, t2, (ord16(x[h] & 0xFFFFu) << 16) | (id - 2 * h));
-        take(t1, t2, (ord16(x[h] >> 16) << 16) | (id - 2 * h - 1));
-      }
-    }
+  for (; v + kThreads < n_vec; v += 2 * kThreads) {
+    const v4u w0 = __builtin_nontemporal_load(&vp[v]);
+    const v4u w1 = __builtin_nontemporal_load(&vp[v + kThreads]);
+    take8(t1, t2, w0, c0 + 8 * v);
+    take8(t1, t2, w1, c0 + 8 * (v + kThreads));
   }
-  for (; v < n_vec; v += kThreads) {
-    const uint4 w = vp[v];
-    const uint32_t id = 0xFFFFu - (c0 + 8 * v);
-    const uint32_t x[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-    for (int h = 0; h < 4; ++h) {
-      take(t1, t2, (ord16(x[h] & 0xFFFFu) << 16) | (id - 2 * h));
-      take(t1, t2, (ord16(x[h] >> 16) << 16) | (id - 2 * h - 1));
-    }
-  }
+  for (; v < n_vec; v += kThreads) take8(t1, t2, __builtin_nontemporal_load(&vp[v]), c0 + 8 * v);
   // Columns past the last whole vector (only in a shard's last slice).
   const uint32_t c_tail = c0 + 8 * n_vec;
   if (tid < c1 - c_tail) {
@@ -126,7 +128,6 @@ __global__ __launch_bounds__(kThreads) void argmax_kernel(Shards sh, uint32_t sp
 
   wave_reduce(t1, t2);
   __shared__ uint32_t lds1[kWaves], lds2[kWaves];
-  __shared__ uint32_t last;
   const uint32_t wave = tid / 64, lane = tid % 64;
   if (lane == 63) {
     lds1[wave] = t1;
@@ -137,27 +138,18 @@ __global__ __launch_bounds__(kThreads) void argmax_kernel(Shards sh, uint32_t sp
     uint32_t a1 = lds1[0], a2 = lds2[0];
 #pragma unroll
     for (int w = 1; w < kWaves; ++w) merge(a1, a2, lds1[w], lds2[w]);
-    __hip_atomic_store(&partials[blockIdx.x], ((uint64_t)a1 << 32) | a2, __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
-    // Release our partial, then count; the workgroup that brings the count to
-    // per_row sees every other partial of the row.
-    const uint32_t prev =
-        __hip_atomic_fetch_add(&counters[row], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    last = (prev == per_row - 1);
+    partials[blockIdx.x] = ((uint64_t)a1 << 32) | a2;
   }
-  __syncthreads();
-  if (!last || wave != 0) return;
+}
 
-  // Fold (wave 0 of the row's last workgroup): lane i holds partial i; lanes
-  // [0, splits) are shard 0's slices, [splits, 2 * splits) shard 1's.
-  // Every workgroup of the row has published, so nothing else touches these
-  // partials in this call: read them, then clear them for the next call.
-  uint64_t p = 0;
-  if (lane < per_row) {
-    uint64_t *slot = &partials[(uint64_t)row * per_row + lane];
-    p = __hip_atomic_load(slot, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(slot, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
+// One wavefront per row: lane i holds partial i of the row; lanes
+// [0, splits) are shard 0's slices, [splits, 2 * splits) shard 1's.
+template <int MODE>
+__global__ __launch_bounds__(64) void argmax_fold_kernel(Shards sh, uint32_t splits, const uint64_t *partials,
+                                                         void *out) {
+  const uint32_t row = blockIdx.x, lane = threadIdx.x;
+  const uint32_t per_row = 2 * splits;
+  const uint64_t p = lane < per_row ? partials[(uint64_t)row * per_row + lane] : 0;
   const bool in0 = lane < splits;
   uint32_t a1 = in0 ? (uint32_t)(p >> 32) : 0, a2 = in0 ? (uint32_t)p : 0;
   uint32_t b1 = in0 ? 0 : (uint32_t)(p >> 32), b2 = in0 ? 0 : (uint32_t)p;
@@ -189,6 +181,8 @@ __global__ __launch_bounds__(kThreads) void argmax_kernel(Shards sh, uint32_t sp
     return x.gid < y.gid;
   };
   const Rec x1 = rec(a1, 0), x2 = rec(a2, 0), y1 = rec(b1, 1), y2 = rec(b2, 1);
+  // Both shards hold at least one column, so both top1 records exist and the
+  // chosen top2 (the loser's top1 if nothing beats it) always exists too.
   const bool x_wins = before(x1, y1);
   const Rec &top1 = x_wins ? x1 : y1;
   const Rec &lose1 = x_wins ? y1 : x1;
@@ -210,8 +204,6 @@ __global__ __launch_bounds__(kThreads) void argmax_kernel(Shards sh, uint32_t sp
     r.reserved = 0;
     reinterpret_cast<xfer_top2 *>(out)[row] = r;
   }
-  // Leave the counter at zero for the next call on this workspace.
-  __hip_atomic_store(&counters[row], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 uint32_t round_up8(uint32_t x) { return (x + 7u) & ~7u; }
@@ -229,12 +221,8 @@ uint32_t argmax_splits(uint32_t rows, uint32_t ncols0, uint32_t ncols1) {
   return (uint32_t)want;
 }
 
-// Layout: counters u32[rows] (padded to 16 bytes), then partials
-// u64[rows][2][splits].
-uint64_t argmax_workspace_bytes(uint32_t rows, uint32_t splits) {
-  const uint64_t counters = ((uint64_t)rows * 4 + 15) & ~15ull;
-  return counters + (uint64_t)rows * 2 * splits * 8;
-}
+// Layout: partials u64[rows][2][splits].
+uint64_t argmax_workspace_bytes(uint32_t rows, uint32_t splits) { return (uint64_t)rows * 2 * splits * 8; }
 
 hipError_t launch_argmax(ArgmaxShard s0, ArgmaxShard s1, uint32_t rows, int mode, void *out, void *workspace,
                          uint32_t splits, hipStream_t stream) {
@@ -247,13 +235,13 @@ hipError_t launch_argmax(ArgmaxShard s0, ArgmaxShard s1, uint32_t rows, int mode
     sh.off[i] = in[i].col_offset;
     sh.slice[i] = round_up8((in[i].ncols + splits - 1) / splits);
   }
-  uint32_t *counters = reinterpret_cast<uint32_t *>(workspace);
-  uint64_t *partials = reinterpret_cast<uint64_t *>(reinterpret_cast<uint8_t *>(workspace) +
-                                                    (((uint64_t)rows * 4 + 15) & ~15ull));
-  const dim3 grid(rows * 2 * splits);
+  uint64_t *partials = reinterpret_cast<uint64_t *>(workspace);
+  hipError_t e = launch(argmax_scan_kernel, dim3(rows * 2 * splits), dim3(kThreads), 0, stream, sh, splits, partials);
+  if (e != hipSuccess) return e;
+  const uint64_t *cp = partials;
   if (mode == XFER_ARGMAX)
-    return launch(argmax_kernel<XFER_ARGMAX>, grid, dim3(kThreads), 0, stream, sh, splits, out, partials, counters);
-  return launch(argmax_kernel<XFER_TOP2>, grid, dim3(kThreads), 0, stream, sh, splits, out, partials, counters);
+    return launch(argmax_fold_kernel<XFER_ARGMAX>, dim3(rows), dim3(64), 0, stream, sh, splits, cp, out);
+  return launch(argmax_fold_kernel<XFER_TOP2>, dim3(rows), dim3(64), 0, stream, sh, splits, cp, out);
 }
 
 }  // namespace xfer

@@ -42,16 +42,21 @@ hipError_t launch_argmax(ArgmaxShard s0, ArgmaxShard s1, uint32_t rows, int mode
 
 // ---- run-table gather / scatter (runs_copy.hip)
 struct PlanView {
-  const uint32_t *tile_run;  // [n_lanes][n_tiles + 1]
-  const uint32_t *run_start; // [n_runs]
-  const uint64_t *run_base;  // [n_runs]
-  const int64_t *run_stride; // [n_runs]
-  uint32_t n_lanes, n_blocks, n_tiles, tile_blocks;
+  const uint32_t *group_run;  // [n_lanes][n_groups + 1]
+  const uint32_t *run_start;  // [n_runs]
+  const uint64_t *run_base;   // [n_runs]
+  const int64_t *run_stride;  // [n_runs]
+  uint32_t n_lanes, n_blocks;
+  uint32_t tile_blocks;       // blocks per workgroup; divides group_blocks
+  uint32_t n_tiles;           // per lane
+  uint32_t group_blocks;      // blocks per index entry
+  uint32_t n_groups;          // per lane
   uint64_t seg_bytes;
-  uint32_t vps;       // 16-byte vectors per segment, <= kMaxSegVectors
-  uint32_t vps_log2;  // log2(vps) if vps is a power of two, else 32
+  uint32_t vps;               // 16-byte vectors per segment, <= kMaxSegVectors
+  uint32_t vps_log2;          // log2(vps) if vps is a power of two, else 32
 };
-constexpr uint32_t kMaxTileBlocks = 64;
+constexpr uint32_t kMaxGroupBlocks = 32;
+constexpr uint32_t kMaxTileBlocks = 32;
 constexpr uint32_t kMaxSegVectors = 1u << 16;  // 1 MiB segments
 hipError_t launch_gather(const PlanView &p, void *staging, hipStream_t stream);
 hipError_t launch_scatter(const PlanView &p, const void *staging, hipStream_t stream);

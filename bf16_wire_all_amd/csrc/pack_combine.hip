@@ -9,16 +9,39 @@
 //     512 B of BF16): fully coalesced 128-bit / 64-bit accesses;
 //   - each thread issues UNROLL independent loads before its first store, so
 //     enough bytes are in flight per CU to cover HBM latency;
-//   - a grid-stride loop over a grid sized to a few waves of workgroups per
-//     CU, so large inputs do not pay per-workgroup launch overhead.
+//   - loads and stores carry the nontemporal hint: each byte is touched once
+//     (cold 2048 x 5120 pack on MI355X: 4.5 TB/s with it, 2.5 TB/s without);
+//   - a grid-stride loop over a grid capped at 32 workgroups per CU, so
+//     large inputs do not pay per-workgroup launch overhead.
 #include "internal.h"
 
 namespace xfer {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kUnroll = 4;
-constexpr uint32_t kMaxGrid = 256 * 8;  // 8 workgroups per CU on 256 CUs
+constexpr int kUnroll = 2;
+constexpr uint32_t kMaxGrid = 256 * 32;  // 32 workgroups per CU on 256 CUs
+
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+typedef unsigned int v2u __attribute__((ext_vector_type(2)));
+template <typename T>
+__device__ __forceinline__ T nt_load(const T *p) {
+  return __builtin_nontemporal_load(p);
+}
+template <typename T>
+__device__ __forceinline__ void nt_store(T *p, T v) {
+  __builtin_nontemporal_store(v, p);
+}
+__device__ __forceinline__ uint4 ld(const uint4 *p) {
+  const v4u v = nt_load(reinterpret_cast<const v4u *>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint2 ld(const uint2 *p) {
+  const v2u v = nt_load(reinterpret_cast<const v2u *>(p));
+  return make_uint2(v.x, v.y);
+}
+__device__ __forceinline__ void st(uint4 *p, uint4 v) { nt_store(reinterpret_cast<v4u *>(p), v4u{v.x, v.y, v.z, v.w}); }
+__device__ __forceinline__ void st(uint2 *p, uint2 v) { nt_store(reinterpret_cast<v2u *>(p), v2u{v.x, v.y}); }
 
 // Round-to-nearest-even of an F32 bit pattern to BF16 (in the low 16 bits).
 // Adding 0x7FFF plus the lowest kept bit carries into the kept bits exactly
@@ -77,18 +100,18 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(const uint4 *__restrict_
   for (; q + (kUnroll - 1) * stride < n_quads; q += kUnroll * stride) {
     uint4 v[kUnroll];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) v[u] = src[q + u * stride];
+    for (int u = 0; u < kUnroll; ++u) v[u] = ld(&src[q + u * stride]);
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       uint64_t d = q + u * stride + slot0_q;
       if (d >= ring_quads) d -= ring_quads;
-      ring[d] = pack_quad(v[u]);
+      st(&ring[d], pack_quad(v[u]));
     }
   }
   for (; q < n_quads; q += stride) {
     uint64_t d = q + slot0_q;
     if (d >= ring_quads) d -= ring_quads;
-    ring[d] = pack_quad(src[q]);
+    st(&ring[d], pack_quad(ld(&src[q])));
   }
 }
 
@@ -111,25 +134,24 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const uint2 *a, const
     uint2 va[kUnroll], vb[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      va[u] = a[q + u * stride];
-      vb[u] = b[q + u * stride];
+      va[u] = ld(&a[q + u * stride]);
+      vb[u] = ld(&b[q + u * stride]);
     }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const uint4 s = sum_quad(va[u], vb[u]);
-      if (MODE == XFER_OUT_F32) {
-        reinterpret_cast<uint4 *>(out)[q + u * stride] = s;
-      } else {
-        reinterpret_cast<uint2 *>(out)[q + u * stride] = pack_quad(s);
-      }
+      if (MODE == XFER_OUT_F32)
+        st(&reinterpret_cast<uint4 *>(out)[q + u * stride], s);
+      else
+        st(&reinterpret_cast<uint2 *>(out)[q + u * stride], pack_quad(s));
     }
   }
   for (; q < n_quads; q += stride) {
-    const uint4 s = sum_quad(a[q], b[q]);
+    const uint4 s = sum_quad(ld(&a[q]), ld(&b[q]));
     if (MODE == XFER_OUT_F32)
-      reinterpret_cast<uint4 *>(out)[q] = s;
+      st(&reinterpret_cast<uint4 *>(out)[q], s);
     else
-      reinterpret_cast<uint2 *>(out)[q] = pack_quad(s);
+      st(&reinterpret_cast<uint2 *>(out)[q], pack_quad(s));
   }
 }
 

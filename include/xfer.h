@@ -20,9 +20,10 @@
  *     `stream`: they never allocate, never synchronise and never block.
  *     xfer_runs_prepare is the one blocking set-up call.
  *   - Every call checks all its arguments on the host first.  On any status
- *     other than XFER_OK nothing has been enqueued and no output byte has
- *     been written; the outputs of a failed call must not be read.
- *     XFER_E_DEVICE reports a launch the runtime refused.
+ *     other than XFER_OK and XFER_E_DEVICE nothing has been enqueued and no
+ *     output byte has been written.  XFER_E_DEVICE reports a launch or copy
+ *     the HIP runtime refused; work enqueued before it may still run.  The
+ *     outputs of a failed call must not be read.
  *   - Empty work (n == 0, rows == 0, an empty chunk range, an empty table) is
  *     XFER_OK with nothing enqueued.
  *   - Every buffer a kernel streams through, and every row start and segment
@@ -157,9 +158,10 @@ typedef struct {
  *   out        (device) xfer_max_idx[rows] (XFER_ARGMAX) or
  *              xfer_top2[rows] (XFER_TOP2).
  *   workspace  (device) at least xfer_argmax_workspace_bytes(rows, s0->ncols,
- *              s1->ncols) bytes, 16-byte aligned, ZERO-FILLED before its first
- *              use; every successful call leaves it zero-filled again.  Calls
- *              that run concurrently must use different workspaces.
+ *              s1->ncols) bytes, 16-byte aligned, any contents: the call writes
+ *              per-slice partial records there and reads them back (it needs
+ *              no initialisation and its contents afterwards are unspecified).
+ *              Calls that may run concurrently must use different workspaces.
  *
  * Errors: XFER_E_INVAL for NULL or misaligned pointers (ptr and ld * 2 must
  * be multiples of 16), different row counts, ncols == 0, shards whose id
@@ -257,8 +259,10 @@ typedef struct {
   uint32_t is_dst;
   uint32_t tile_blocks;      /* private from here on                   */
   uint32_t n_tiles;
+  uint32_t group_blocks;
+  uint32_t n_groups;
   uint32_t magic;
-  uint64_t off_tile_run, off_run_start, off_run_base, off_run_stride;
+  uint64_t off_group_run, off_run_start, off_run_base, off_run_stride;
 } xfer_runs_plan;
 
 /* Device bytes xfer_runs_prepare needs for table t (0 if t is NULL). */

@@ -9,7 +9,7 @@ import pytest
 import bf16_wire_all_amd as x
 import datagen as dg
 import oracle
-from tests.gpu_util import down, random_bf16, say, up, zeros
+from tests.gpu_util import down, filled, random_bf16, say, up, zeros
 
 pytestmark = pytest.mark.gpu
 
@@ -31,14 +31,13 @@ def _check_matrix(logits, split, n1=None, calls=2):
     dl = up(logits)
     s0 = x.shard(dl.data_ptr(), cols, rows, split, 0)
     s1 = x.shard(dl.data_ptr() + 2 * split, cols, rows, n1, split)
-    ws = zeros(x.argmax_workspace_bytes(rows, split, n1))
+    # the workspace needs no initialisation: start it full of garbage
+    ws = filled(x.argmax_workspace_bytes(rows, split, n1), 0xFF)
     for mode, rec in MODES:
         want = oracle.argmax_merge(logits, split, mode, ncols1=n1)
         for _ in range(calls):
             got = _run(dl, s0, s1, rows, ws, mode, rec)
             assert got.tobytes() == want.tobytes(), (mode, np.nonzero(got != want)[0][:5])
-    # the workspace is back to zero after every call
-    assert not np.any(down(ws))
     return want
 
 
