@@ -40,10 +40,10 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def algorithmic_bytes():
-    n = TOKENS * HIDDEN
+def algorithmic_bytes(tokens=TOKENS, extra_gathers=()):
+    n = tokens * HIDDEN
     kv = N_BLOCKS * N_SLOTS * 2 * SEG
-    return {
+    ab = {
         "pack_rank0": 6 * n,                 # 4 B read + 2 B written per element
         "pack_rank1": 6 * n,
         "gather": 2 * kv,                    # every segment read once and written once
@@ -51,6 +51,9 @@ def algorithmic_bytes():
         "argmax_top2": ROWS * VOCAB * 2 + ROWS * 16,
         "combine_f32": 8 * n,                # 2 + 2 B read, 4 B written per element
     }
+    for name in extra_gathers:
+        ab[name] = 2 * kv
+    return ab
 
 
 def source_hash(name):
@@ -74,9 +77,13 @@ def measured_traffic(kernel_file, key):
 
 
 class Workload:
-    """Device buffers of one step, filled from the seeded generators."""
+    """Device buffers of one step, filled from the seeded generators.
 
-    def __init__(self, dev):
+    tokens: rows of the F32 partials (x 5120); shuffled: blocks allocated in a
+    seeded random order, so every lane breaks into many runs (the greedy
+    table, and a second table with one run per segment, are both gathered)."""
+
+    def __init__(self, dev, tokens=TOKENS, shuffled=False):
         import numpy as np
         import torch
 
@@ -84,12 +91,14 @@ class Workload:
         import datagen as dg
 
         self.x, self.torch, self.np = x, torch, np
-        n = TOKENS * HIDDEN
+        self.tokens, self.shuffled = tokens, shuffled
+        n = tokens * HIDDEN
         self.n = n
         self.n_chunks = -(-n // (CHUNK // 2))
         log("bench: generating inputs")
-        self.a_host = dg.prompt_partial(n, dg.seed_for(2, 0, TOKENS))
-        self.b_host = dg.prompt_partial(n, dg.seed_for(2, 1, TOKENS))
+        cfg = 5 if shuffled else 2
+        self.a_host = dg.prompt_partial(n, dg.seed_for(cfg, 0, tokens))
+        self.b_host = dg.prompt_partial(n, dg.seed_for(cfg, 1, tokens))
         self.a = torch.from_numpy(self.a_host).to(dev)
         self.b = torch.from_numpy(self.b_host).to(dev)
         # BF16 bit patterns are held in int16 tensors (2-byte elements)
@@ -109,7 +118,8 @@ class Workload:
         rb = dg.region_bytes_for(N_BLOCKS, N_SLOTS, SEG)
         self.regions = [torch.empty(rb, dtype=torch.uint8, device=dev) for _ in range(2)]
         bases = [r.data_ptr() for r in self.regions]
-        self.src_addrs = dg.kv_src_addrs(N_BLOCKS, N_SLOTS, SEG, bases)
+        pos = dg.permutation(N_BLOCKS, dg.seed_for(5, 0, 1)) if shuffled else None
+        self.src_addrs = dg.kv_src_addrs(N_BLOCKS, N_SLOTS, SEG, bases, pos=pos)
         self.region_hosts = []
         for i, r in enumerate(self.regions):
             h = np.empty(rb, np.uint8)
@@ -119,6 +129,12 @@ class Workload:
         self.src_table = x.runs_encode(self.src_addrs, SEG)
         self.src_plan_buf = torch.zeros(x.runs_plan_bytes(self.src_table), dtype=torch.uint8, device=dev)
         self.src_plan = x.runs_prepare(self.src_table, [(b, rb) for b in bases], False, self.src_plan_buf)
+        self.seg_plan = None
+        if shuffled:
+            # the unencoded worst case: one run per segment
+            self.seg_table = x.runs_encode(self.src_addrs, SEG, max_count=1)
+            self.seg_plan_buf = torch.zeros(x.runs_plan_bytes(self.seg_table), dtype=torch.uint8, device=dev)
+            self.seg_plan = x.runs_prepare(self.seg_table, [(b, rb) for b in bases], False, self.seg_plan_buf)
         self.staging = torch.empty(2 * N_SLOTS * N_BLOCKS * SEG, dtype=torch.uint8, device=dev)
         self.dst = torch.full((N_BLOCKS * N_SLOTS * DST_SLOT_STRIDE,), 0xA5, dtype=torch.uint8, device=dev)
         self.dst_addrs = dg.kv_dst_addrs(N_BLOCKS, N_SLOTS, SEG, self.dst.data_ptr(), DST_SLOT_STRIDE)
@@ -133,22 +149,30 @@ class Workload:
         x = self.x
         n, nc = self.n, self.n_chunks
         ra, rb = self.ring_a, self.ring_b
-        return [
+        ks = [
             ("pack_rank0", lambda: x.pack_bf16(self.a, ra, CHUNK, 0, nc)),
             ("pack_rank1", lambda: x.pack_bf16(self.b, rb, CHUNK, 0, nc)),
             ("gather", lambda: x.gather_runs(self.src_plan, self.staging)),
+        ]
+        if self.seg_plan is not None:
+            ks.append(("gather_per_segment", lambda: x.gather_runs(self.seg_plan, self.staging)))
+        ks += [
             ("scatter", lambda: x.scatter_runs(self.staging, self.dst_plan)),
             ("argmax_top2", lambda: x.argmax_merge(self.s0, self.s1, x.TOP2, self.top2, self.ws)),
             ("combine_f32", lambda: x.combine2(ra[:n], rb[:n], self.sum, x.OUT_F32)),
         ]
+        return ks
+
+    def algorithmic_bytes(self):
+        return algorithmic_bytes(self.tokens, ("gather_per_segment",) if self.seg_plan is not None else ())
 
 
-def run_gpu(steps, warmup):
+def run_gpu(steps, warmup, workload):
     import torch
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    w = Workload(dev)
+    w = Workload(dev, **WORKLOADS[workload]["args"])
     ks = w.kernels()
     log(f"bench: warmup {warmup} steps")
     for _ in range(warmup):
@@ -193,13 +217,19 @@ def cpu_baseline(w, budget_s=12.0):
     staging = np.ones(2 * N_SLOTS * N_BLOCKS * SEG, np.uint8)
     dst = np.full(N_BLOCKS * N_SLOTS * DST_SLOT_STRIDE, 0xA5, np.uint8)
     dst_regions = [(w.dst.data_ptr(), dst)]
-    step_bytes = sum(algorithmic_bytes().values())
+    step_bytes = sum(w.algorithmic_bytes().values())
+    seg_t = None
+    if w.seg_plan is not None:
+        seg_t = oracle.RunTable(w.seg_table.runs_per_lane, w.seg_table.run_base, w.seg_table.run_stride,
+                                w.seg_table.run_count, N_BLOCKS)
     reps, t_total = 0, 0.0
     while t_total < budget_s and reps < 50:
         t0 = time.perf_counter()
         oracle.pack(w.a_host, ring_a.size, ce, 0, w.n_chunks, ring=ring_a)
         oracle.pack(w.b_host, ring_b.size, ce, 0, w.n_chunks, ring=ring_b)
         oracle.gather(src_t, SEG, regions, staging=staging)
+        if seg_t is not None:
+            oracle.gather(seg_t, SEG, regions, staging=staging)
         oracle.scatter(dst_t, SEG, dst_regions, staging)
         oracle.argmax_merge(w.logits_host, SPLIT, 1)
         oracle.combine2(ring_a[:n], ring_b[:n], 0)
@@ -213,6 +243,24 @@ def cpu_baseline(w, budget_s=12.0):
         "sample": f"{reps} full steps of the same workload (same sizes and inputs), single-threaded C oracle, "
                   f"{t_total:.1f} s; host has {os.cpu_count()} logical CPUs",
     }
+
+
+WORKLOADS = {
+    "step": {
+        "args": {"tokens": TOKENS, "shuffled": False},
+        "describe": "transfer hot path: pack x2 + combine2 (2048x5120 F32 partials, 512 KiB BF16 chunks), "
+                    "argmax merge (16x129280 BF16, split at 64768, top2), gather+scatter by run table "
+                    "(1000 blocks x 288 slots x 2 x 4 KiB, one run per lane)",
+        "roofline_kernel": ("gather", "gather_runs (paged K/V, 576 runs)", "gather_dense"),
+    },
+    "fragmented": {
+        "args": {"tokens": 16384, "shuffled": True},
+        "describe": "fragmented transfer: pack x2 + combine2 (16384x5120 F32 partials), argmax merge "
+                    "(16x129280), gather of 1000 x 288 x 2 x 4 KiB with a shuffled block order by the greedy "
+                    "run table (288,000 runs) and by one run per segment (576,000 runs), scatter",
+        "roofline_kernel": ("gather", "gather_runs (shuffled blocks, 288,000 runs)", "gather_fragmented"),
+    },
+}
 
 
 def calib_copy(gib=1, reps=5):
@@ -234,6 +282,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", choices=sorted(WORKLOADS), default="step",
+                    help="step (default): the bench line; fragmented: the shuffled-layout / large-combine shapes")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy", action="store_true", help="run only the copy used to scale PMC readings")
     args = ap.parse_args()
@@ -247,8 +297,9 @@ def main():
     if args.steps < 1:
         sys.exit("--steps must be >= 1")
 
-    w, elapsed, kms = run_gpu(args.steps, args.warmup)
-    ab = algorithmic_bytes()
+    wl = WORKLOADS[args.workload]
+    w, elapsed, kms = run_gpu(args.steps, args.warmup, args.workload)
+    ab = w.algorithmic_bytes()
     step_bytes = sum(ab.values())
     ms_per_step = elapsed / args.steps * 1e3
     value = step_bytes * args.steps / elapsed / 1e9
@@ -257,10 +308,11 @@ def main():
         gbs = ab[name] / (ms * 1e-3) / 1e9
         kernels[name] = {"us": round(ms * 1e3, 2), "bytes": ab[name], "GBps": round(gbs, 1),
                          "frac_of_peak": round(gbs / PEAK_HBM_GBS, 4)}
-    g_gbs = ab["gather"] / (kms["gather"] * 1e-3) / 1e9
-    roofline = {"kernel": "gather_runs (paged K/V, 576 runs)", "bound": "hbm", "achieved": round(g_gbs, 1),
+    rk, rk_label, rk_key = wl["roofline_kernel"]
+    g_gbs = ab[rk] / (kms[rk] * 1e-3) / 1e9
+    roofline = {"kernel": rk_label, "bound": "hbm", "achieved": round(g_gbs, 1),
                 "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(g_gbs / PEAK_HBM_GBS, 4),
-                "traffic": measured_traffic("runs_copy.hip", "gather_dense")}
+                "traffic": measured_traffic("runs_copy.hip", rk_key)}
     line = {
         "metric": "achieved HBM GB/s (and % of peak) for pack+combine and run-table segment gather",
         "value": round(value, 1),
@@ -275,9 +327,7 @@ def main():
         "dtype": "f32+bf16",
         "data": "synthetic",
         "config": {
-            "workload": "transfer hot path: pack x2 + combine2 (2048x5120 F32 partials, 512 KiB BF16 chunks), "
-                        "argmax merge (16x129280 BF16, split at 64768, top2), gather+scatter by run table "
-                        "(1000 blocks x 288 slots x 2 x 4 KiB, one run per lane)",
+            "workload": wl["describe"],
             "step_bytes": step_bytes,
             "parallelism": "single GPU; both ranks emulated in one HBM",
         },
@@ -287,7 +337,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": None,
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.workload == "step":
         log("bench: cpu baseline (oracle)")
         line["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(line), flush=True)
