@@ -26,7 +26,8 @@ ARGMAX, TOP2 = 0, 1
 EXPORTED = [
     "xfer_status_str", "xfer_pack_bf16", "xfer_combine2", "xfer_argmax_workspace_bytes",
     "xfer_argmax_merge", "xfer_runs_encode", "xfer_runs_validate", "xfer_runs_plan_bytes",
-    "xfer_runs_prepare", "xfer_gather_runs", "xfer_scatter_runs",
+    "xfer_runs_prepare", "xfer_gather_runs", "xfer_scatter_runs", "xfer_allreduce2_event_id",
+    "xfer_allreduce2_schedule", "xfer_events_create", "xfer_events_destroy", "xfer_allreduce2_streamed",
 ]
 
 
@@ -45,6 +46,19 @@ class RunTableC(ctypes.Structure):
     _fields_ = [("n_lanes", ctypes.c_uint32), ("n_blocks", ctypes.c_uint32), ("seg_bytes", ctypes.c_uint64),
                 ("n_runs", ctypes.c_uint64), ("runs_per_lane", ctypes.c_void_p), ("run_base", ctypes.c_void_p),
                 ("run_stride", ctypes.c_void_p), ("run_count", ctypes.c_void_p)]
+
+
+class Op(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_uint32), ("rank", ctypes.c_uint32), ("chunk", ctypes.c_uint32),
+                ("slot", ctypes.c_uint32), ("stream", ctypes.c_uint32), ("n_waits", ctypes.c_uint32),
+                ("wait_event", ctypes.c_uint32 * 2), ("record_event", ctypes.c_uint32)]
+
+
+class AllReduce2Desc(ctypes.Structure):
+    _fields_ = [("src", ctypes.c_void_p * 2), ("send", ctypes.c_void_p * 2), ("recv", ctypes.c_void_p * 2),
+                ("out", ctypes.c_void_p * 2), ("n", ctypes.c_size_t), ("chunk_bytes", ctypes.c_size_t),
+                ("ring_bytes", ctypes.c_size_t), ("out_mode", ctypes.c_int), ("compute", ctypes.c_void_p * 2),
+                ("wire", ctypes.c_void_p * 2), ("events", ctypes.c_void_p)]
 
 
 class Region(ctypes.Structure):
@@ -95,6 +109,16 @@ def lib():
         L.xfer_gather_runs.restype = I
         L.xfer_scatter_runs.argtypes = [P, S, ctypes.POINTER(RunsPlan), P]
         L.xfer_scatter_runs.restype = I
+        L.xfer_allreduce2_event_id.argtypes = [U32, U32, U32, U32]
+        L.xfer_allreduce2_event_id.restype = U32
+        L.xfer_allreduce2_schedule.argtypes = [U32, U32, ctypes.POINTER(Op), S, ctypes.POINTER(S)]
+        L.xfer_allreduce2_schedule.restype = I
+        L.xfer_events_create.argtypes = [P, I]
+        L.xfer_events_create.restype = I
+        L.xfer_events_destroy.argtypes = [P, I]
+        L.xfer_events_destroy.restype = I
+        L.xfer_allreduce2_streamed.argtypes = [ctypes.POINTER(AllReduce2Desc)]
+        L.xfer_allreduce2_streamed.restype = I
         _lib = L
     return _lib
 
@@ -279,3 +303,65 @@ def gather_runs_raw(plan: RunsPlan, staging_ptr: int, staging_bytes: int, stream
 
 def scatter_runs_raw(staging_ptr: int, staging_bytes: int, plan: RunsPlan, stream=None) -> int:
     return lib().xfer_scatter_runs(staging_ptr, staging_bytes, ctypes.byref(plan), _stream(stream))
+
+
+# ------------------------------------------------ streamed two-rank all-reduce
+
+OP_PACK, OP_WIRE, OP_COMBINE = 0, 1, 2
+EV_PACKED, EV_SENT, EV_COMBINED = 0, 1, 2
+
+
+def allreduce2_event_id(kind: int, rank: int, slot: int, R: int) -> int:
+    return int(lib().xfer_allreduce2_event_id(kind, rank, slot, R))
+
+
+def allreduce2_schedule(n_chunks: int, R: int):
+    """The driver's operation list (host only) as a list of dicts."""
+    cap = 6 * n_chunks
+    ops = (Op * max(1, cap))()
+    n = ctypes.c_size_t(0)
+    _check(lib().xfer_allreduce2_schedule(n_chunks, R, ops, cap, ctypes.byref(n)), "xfer_allreduce2_schedule")
+    return [{"kind": o.kind, "rank": o.rank, "chunk": o.chunk, "slot": o.slot, "stream": o.stream,
+             "waits": list(o.wait_event[:o.n_waits]), "record": o.record_event} for o in ops[:n.value]]
+
+
+class Events:
+    """n HIP events for the streamed driver (created recorded and complete)."""
+
+    def __init__(self, n: int):
+        self.n = n
+        self.array = (ctypes.c_void_p * max(1, n))()
+        _check(lib().xfer_events_create(self.array, n), "xfer_events_create")
+
+    def close(self):
+        if self.array is not None:
+            lib().xfer_events_destroy(self.array, self.n)
+            self.array = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def allreduce2_streamed(src, send, recv, out, chunk_bytes: int, mode: int, compute, wire, events: Events,
+                        ring_bytes: int | None = None) -> int:
+    """src, send, recv, out: pairs of CUDA tensors (rank 0, rank 1); compute,
+    wire: pairs of torch streams (or raw stream handles).  Returns the status."""
+    def h(s):
+        return s.cuda_stream if hasattr(s, "cuda_stream") else int(s)
+    d = AllReduce2Desc()
+    for r in range(2):
+        d.src[r] = _dev(src[r])
+        d.send[r] = _dev(send[r])
+        d.recv[r] = _dev(recv[r])
+        d.out[r] = _dev(out[r])
+        d.compute[r] = h(compute[r])
+        d.wire[r] = h(wire[r])
+    d.n = src[0].numel() * src[0].element_size() // 4     # F32 elements
+    d.chunk_bytes = chunk_bytes
+    d.ring_bytes = send[0].numel() * send[0].element_size() if ring_bytes is None else ring_bytes
+    d.out_mode = mode
+    d.events = ctypes.cast(events.array, ctypes.c_void_p)
+    return lib().xfer_allreduce2_streamed(ctypes.byref(d))

@@ -1,0 +1,184 @@
+// Streamed two-rank all-reduce of the copy-engine page ("Change"): per chunk,
+// pack on each rank's compute stream, copy into the peer's receive ring on
+// the rank's wire stream, combine on the compute stream; R slots alternate;
+// streams are ordered by events only.
+//
+// The schedule is produced by one generator, used both by
+// xfer_allreduce2_schedule (so the ordering can be checked on the host) and by
+// the executor, which issues each operation as it is generated (no host
+// allocation in the call).
+//
+// Hazards per slot s of rank r (chunk c reuses the slot of chunk c - R):
+//   send[r][s]  written by PACK r c; read by WIRE r c and COMBINE r c.
+//               PACK r c waits SENT[r][s] (the wire copy of chunk c - R is
+//               done); COMBINE r c - R precedes it on the same stream.
+//   recv[1-r][s] written by WIRE r c; read by COMBINE 1-r c.
+//               WIRE r c waits PACKED[r][s] (its input is ready) and
+//               COMBINED[1-r][s] (the peer's sum of chunk c - R is done);
+//               COMBINE 1-r c waits SENT[r][s].
+// Events are created already recorded (complete), so the waits of the first
+// R chunks of a call are satisfied at once, or wait for a previous call that
+// used the same events and rings.
+#include <cstring>
+
+#include "internal.h"
+
+namespace {
+
+constexpr uint32_t kStreams = 4;  // compute 0, compute 1, wire 0, wire 1
+
+uint32_t event_id(uint32_t kind, uint32_t rank, uint32_t slot, uint32_t R) { return (kind * 2 + rank) * R + slot; }
+
+// Calls visit(op) for every operation in issue order.
+template <typename Visit>
+bool for_each_op(uint32_t n_chunks, uint32_t R, Visit &&visit) {
+  for (uint32_t c = 0; c < n_chunks; ++c) {
+    const uint32_t s = c % R;
+    for (uint32_t r = 0; r < 2; ++r) {
+      xfer_op op{};
+      op.kind = XFER_OP_PACK;
+      op.rank = r;
+      op.chunk = c;
+      op.slot = s;
+      op.stream = r;
+      op.n_waits = 1;
+      op.wait_event[0] = event_id(XFER_EV_SENT, r, s, R);
+      op.record_event = event_id(XFER_EV_PACKED, r, s, R);
+      if (!visit(op)) return false;
+    }
+    for (uint32_t r = 0; r < 2; ++r) {
+      xfer_op op{};
+      op.kind = XFER_OP_WIRE;
+      op.rank = r;
+      op.chunk = c;
+      op.slot = s;
+      op.stream = 2 + r;
+      op.n_waits = 2;
+      op.wait_event[0] = event_id(XFER_EV_PACKED, r, s, R);
+      op.wait_event[1] = event_id(XFER_EV_COMBINED, 1 - r, s, R);
+      op.record_event = event_id(XFER_EV_SENT, r, s, R);
+      if (!visit(op)) return false;
+    }
+    for (uint32_t r = 0; r < 2; ++r) {
+      xfer_op op{};
+      op.kind = XFER_OP_COMBINE;
+      op.rank = r;
+      op.chunk = c;
+      op.slot = s;
+      op.stream = r;
+      op.n_waits = 1;
+      op.wait_event[0] = event_id(XFER_EV_SENT, 1 - r, s, R);
+      op.record_event = event_id(XFER_EV_COMBINED, r, s, R);
+      if (!visit(op)) return false;
+    }
+  }
+  return true;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+uint32_t xfer_allreduce2_event_id(uint32_t kind, uint32_t rank, uint32_t slot, uint32_t R) {
+  return event_id(kind, rank, slot, R);
+}
+
+int xfer_allreduce2_schedule(uint32_t n_chunks, uint32_t R, xfer_op *ops, size_t cap, size_t *n_ops) {
+  if (R == 0 || !n_ops) return XFER_E_INVAL;
+  const uint64_t need = 6ull * n_chunks;
+  if (need > cap) return XFER_E_RANGE;
+  if (need && !ops) return XFER_E_INVAL;
+  size_t k = 0;
+  for_each_op(n_chunks, R, [&](const xfer_op &op) {
+    ops[k++] = op;
+    return true;
+  });
+  *n_ops = k;
+  return XFER_OK;
+}
+
+int xfer_events_create(hipEvent_t *events, int n) {
+  if (!events || n < 0) return XFER_E_INVAL;
+  for (int i = 0; i < n; ++i) {
+    // Recorded once and completed, so a first wait on it does not block.
+    if (hipEventCreateWithFlags(&events[i], hipEventDisableTiming) != hipSuccess ||
+        hipEventRecord(events[i], nullptr) != hipSuccess) {
+      for (int j = 0; j <= i; ++j)
+        if (events[j]) (void)hipEventDestroy(events[j]);
+      return XFER_E_DEVICE;
+    }
+  }
+  for (int i = 0; i < n; ++i)
+    if (hipEventSynchronize(events[i]) != hipSuccess) return XFER_E_DEVICE;
+  return XFER_OK;
+}
+
+int xfer_events_destroy(hipEvent_t *events, int n) {
+  if (!events || n < 0) return XFER_E_INVAL;
+  int st = XFER_OK;
+  for (int i = 0; i < n; ++i)
+    if (events[i] && hipEventDestroy(events[i]) != hipSuccess) st = XFER_E_DEVICE;
+  return st;
+}
+
+int xfer_allreduce2_streamed(const xfer_allreduce2_desc *d) {
+  if (!d) return XFER_E_INVAL;
+  if (d->out_mode != XFER_OUT_F32 && d->out_mode != XFER_OUT_BF16) return XFER_E_INVAL;
+  if (d->chunk_bytes == 0 || d->chunk_bytes % 16) return XFER_E_INVAL;
+  if (d->ring_bytes == 0 || d->ring_bytes % d->chunk_bytes) return XFER_E_INVAL;
+  const uint64_t R = d->ring_bytes / d->chunk_bytes;
+  if (R > UINT32_MAX / 6) return XFER_E_INVAL;
+  if (d->n == 0) return XFER_OK;
+  if (!d->events) return XFER_E_INVAL;
+  if (d->n > SIZE_MAX / 4) return XFER_E_INVAL;
+  const uint64_t ce = d->chunk_bytes / 2;
+  const uint64_t n_chunks = d->n / ce + (d->n % ce != 0);
+  if (n_chunks > UINT32_MAX) return XFER_E_INVAL;
+  const uint64_t out_esize = d->out_mode == XFER_OUT_F32 ? 4 : 2;
+  struct Buf {
+    const void *p;
+    uint64_t bytes;
+  } bufs[8] = {{d->src[0], 4ull * d->n},      {d->src[1], 4ull * d->n},    {d->send[0], d->ring_bytes},
+               {d->send[1], d->ring_bytes},   {d->recv[0], d->ring_bytes}, {d->recv[1], d->ring_bytes},
+               {d->out[0], out_esize * d->n}, {d->out[1], out_esize * d->n}};
+  for (int i = 0; i < 8; ++i)
+    if (!bufs[i].p || !aligned16(bufs[i].p)) return XFER_E_INVAL;
+  // The sources may alias each other (both read only); nothing else may share a byte.
+  for (int i = 0; i < 8; ++i)
+    for (int j = i + 1; j < 8; ++j) {
+      if (i == 0 && j == 1) continue;
+      const uintptr_t a = (uintptr_t)bufs[i].p, b = (uintptr_t)bufs[j].p;
+      if (a < b + bufs[j].bytes && b < a + bufs[i].bytes) return XFER_E_INVAL;
+    }
+  hipStream_t streams[kStreams] = {d->compute[0], d->compute[1], d->wire[0], d->wire[1]};
+  const uint32_t R32 = (uint32_t)R;
+  hipError_t err = hipSuccess;
+  for_each_op((uint32_t)n_chunks, R32, [&](const xfer_op &op) {
+    hipStream_t st = streams[op.stream];
+    for (uint32_t w = 0; w < op.n_waits; ++w)
+      if ((err = hipStreamWaitEvent(st, d->events[op.wait_event[w]], 0)) != hipSuccess) return false;
+    const uint64_t e0 = (uint64_t)op.chunk * ce;
+    const uint64_t len = (d->n - e0 < ce) ? d->n - e0 : ce;
+    const uint64_t soff = (uint64_t)op.slot * ce;  // element offset of the slot
+    const uint32_t r = op.rank;
+    if (op.kind == XFER_OP_PACK) {
+      err = xfer::launch_pack(d->src[r] + e0, len, d->send[r], R * ce, soff, st);
+    } else if (op.kind == XFER_OP_WIRE) {
+      err = hipMemcpyAsync(d->recv[1 - r] + soff, d->send[r] + soff, len * 2, hipMemcpyDeviceToDevice, st);
+    } else {
+      // rank 0's value first on both ranks
+      const uint16_t *a = (r == 0) ? d->send[0] + soff : d->recv[1] + soff;
+      const uint16_t *b = (r == 0) ? d->recv[0] + soff : d->send[1] + soff;
+      void *o = static_cast<uint8_t *>(d->out[r]) + e0 * out_esize;
+      err = xfer::launch_combine(a, b, len, o, d->out_mode, st);
+    }
+    if (err != hipSuccess) return false;
+    err = hipEventRecord(d->events[op.record_event], st);
+    return err == hipSuccess;
+  });
+  return err == hipSuccess ? XFER_OK : XFER_E_DEVICE;
+}
+
+}  // extern "C"

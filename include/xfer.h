@@ -305,6 +305,90 @@ XFER_API int xfer_gather_runs(const xfer_runs_plan *src_plan, void *staging, siz
 XFER_API int xfer_scatter_runs(const void *staging, size_t staging_bytes, const xfer_runs_plan *dst_plan,
                       hipStream_t stream);
 
+/* -------------------------------------------- streamed two-rank all-reduce */
+
+/*
+ * The copy-engine all-reduce of [CE] "Change", both ranks emulated on one GPU:
+ * per chunk, each rank converts its F32 chunk to BF16 into a slot of its send
+ * ring (xfer_pack_bf16), the chunk crosses the "wire" (a device-to-device copy
+ * into the peer's receive ring, on the sending rank's wire stream), and each
+ * rank sums its own and the peer's chunk in F32 with rank 0's value first
+ * (xfer_combine2), so both ranks get identical bits.  R slots alternate
+ * (R = 2 in [CE]); the streams are ordered by events only and the host never
+ * waits.
+ *
+ * The schedule is a list of operations, each on one of four streams
+ * (compute 0, compute 1, wire 0, wire 1):
+ *   PACK r c       compute r: wait SENT[r][s] of chunk c - R (slot free), pack, record PACKED[r][s]
+ *   WIRE r c       wire r:    wait PACKED[r][s]; wait COMBINED[1-r][s] of chunk c - R (peer slot free);
+ *                             copy send[r] slot s -> recv[1-r] slot s; record SENT[r][s]
+ *   COMBINE r c    compute r: wait SENT[1-r][s]; combine; record COMBINED[r][s]
+ * with s = c mod R.  Every wait is always issued: the events are created
+ * already recorded and complete (xfer_events_create), so the first R chunks
+ * of a call either proceed at once or wait for the previous call that used
+ * the same events and rings.  xfer_allreduce2_schedule returns the list (host
+ * only, no GPU), so the ordering can be checked without running it.
+ */
+enum { XFER_OP_PACK = 0, XFER_OP_WIRE = 1, XFER_OP_COMBINE = 2 };
+enum { XFER_EV_PACKED = 0, XFER_EV_SENT = 1, XFER_EV_COMBINED = 2 };
+
+typedef struct {
+  uint32_t kind;     /* XFER_OP_*                                                  */
+  uint32_t rank;     /* 0 or 1                                                     */
+  uint32_t chunk;
+  uint32_t slot;     /* chunk mod R                                                */
+  uint32_t stream;   /* 0, 1: compute stream of rank 0, 1; 2, 3: wire stream of 0, 1 */
+  uint32_t n_waits;  /* 0..2                                                       */
+  uint32_t wait_event[2]; /* event ids waited on before the operation              */
+  uint32_t record_event;  /* event id recorded after it                            */
+} xfer_op;
+
+/* Event id of (kind, rank, slot): (kind * 2 + rank) * R + slot; 6 * R events. */
+XFER_API uint32_t xfer_allreduce2_event_id(uint32_t kind, uint32_t rank, uint32_t slot, uint32_t R);
+
+/*
+ * xfer_allreduce2_schedule - the operation list for n_chunks chunks and R
+ * slots, in issue order (3 operations per rank per chunk).  ops (host) has
+ * capacity cap; *n_ops receives the count.
+ * Errors: XFER_E_INVAL for R == 0 or NULL pointers, XFER_E_RANGE if cap is
+ * too small.  Host only.
+ */
+XFER_API int xfer_allreduce2_schedule(uint32_t n_chunks, uint32_t R, xfer_op *ops, size_t cap, size_t *n_ops);
+
+/* Create n events without timing, each recorded once on the null stream and
+ * completed before returning; destroy them.  Host resources for the driver
+ * (set-up calls: they may block and allocate runtime objects). */
+XFER_API int xfer_events_create(hipEvent_t *events, int n);
+XFER_API int xfer_events_destroy(hipEvent_t *events, int n);
+
+typedef struct {
+  const float *src[2];    /* (device) rank r's F32 partial, n elements                */
+  uint16_t *send[2];      /* (device) rank r's send ring, ring_bytes                  */
+  uint16_t *recv[2];      /* (device) rank r's receive ring, ring_bytes               */
+  void *out[2];           /* (device) rank r's result: n F32 or n BF16 patterns       */
+  size_t n;
+  size_t chunk_bytes;     /* BF16 bytes per chunk, multiple of 16 (524288 in [CE])    */
+  size_t ring_bytes;      /* R * chunk_bytes                                          */
+  int out_mode;           /* XFER_OUT_F32 or XFER_OUT_BF16                            */
+  hipStream_t compute[2]; /* rank r's conversion and sum stream                       */
+  hipStream_t wire[2];    /* rank r's outgoing copy stream                            */
+  hipEvent_t *events;     /* 6 * R events from xfer_events_create                     */
+} xfer_allreduce2_desc;
+
+/*
+ * xfer_allreduce2_streamed - enqueue the whole schedule; returns without
+ * waiting.  out[0] and out[1] both receive combine2(pack(src[0]),
+ * pack(src[1])) element by element.  The sources must be ready on the compute
+ * streams; the outputs are complete when both compute streams have run past
+ * this call.  A later call with the same rings and events is ordered after
+ * this one by the events themselves.
+ * Errors: XFER_E_INVAL for NULL or misaligned buffers, a bad chunk or ring
+ * size, an unknown out_mode, any two of the ten buffers overlapping, or
+ * fewer than 6 * R events; XFER_E_DEVICE if the runtime refuses an enqueue
+ * (earlier chunks may already be enqueued).
+ */
+XFER_API int xfer_allreduce2_streamed(const xfer_allreduce2_desc *d);
+
 #ifdef __cplusplus
 }
 #endif

@@ -1,0 +1,116 @@
+"""GPU parity of the streamed two-rank all-reduce (xfer_allreduce2_streamed):
+both emulated ranks end with combine2(pack(rank 0), pack(rank 1)) bit for
+bit, equal to the oracle, whatever the relative speed of the four streams.
+Streams are perturbed by spin kernels enqueued ahead of the call, and two
+calls reusing the same rings and events are issued back to back with no host
+synchronisation in between."""
+import numpy as np
+import pytest
+import torch
+
+import bf16_wire_all_amd as x
+import datagen as dg
+import oracle
+from tests.gpu_util import DEV, down, say, up, zeros
+
+pytestmark = pytest.mark.gpu
+
+SPIN = 2_000_000  # cycles of torch.cuda._sleep (about a millisecond)
+
+
+def _want(a, b, mode):
+    pa = oracle.bf16_rne(a.view(np.uint32))
+    pb = oracle.bf16_rne(b.view(np.uint32))
+    return oracle.combine2(pa, pb, mode)
+
+
+class Pair:
+    """Rings, outputs, streams and events of one emulated rank pair."""
+
+    def __init__(self, n, chunk_bytes, R, mode):
+        self.n, self.chunk_bytes, self.R, self.mode = n, chunk_bytes, R, mode
+        self.esize = 4 if mode == x.OUT_F32 else 2
+        self.send = [zeros(R * chunk_bytes) for _ in range(2)]
+        self.recv = [zeros(R * chunk_bytes) for _ in range(2)]
+        self.compute = [torch.cuda.Stream() for _ in range(2)]
+        self.wire = [torch.cuda.Stream() for _ in range(2)]
+        self.events = x.Events(6 * R)
+
+    def run(self, a_dev, b_dev, outs, delays=()):
+        cur = torch.cuda.current_stream()
+        for s in self.compute + self.wire:
+            s.wait_stream(cur)              # the inputs were written on the current stream
+        for which in delays:
+            s = {"c0": self.compute[0], "c1": self.compute[1], "w0": self.wire[0], "w1": self.wire[1]}[which]
+            with torch.cuda.stream(s):
+                torch.cuda._sleep(SPIN)
+        st = x.allreduce2_streamed((a_dev, b_dev), self.send, self.recv, outs, self.chunk_bytes, self.mode,
+                                   self.compute, self.wire, self.events)
+        assert st == x.OK, x.status_str(st)
+        for s in self.compute:
+            cur.wait_stream(s)
+
+
+@pytest.mark.parametrize("R", [1, 2, 3])
+@pytest.mark.parametrize("mode", [x.OUT_F32, x.OUT_BF16])
+def test_small_chunks_all_slot_counts(R, mode):
+    n, chunk = 1001, 64                           # 32 elements per chunk, ragged last chunk
+    a = dg.normal_f32(n, 100 + R, 1.0)
+    b = dg.normal_f32(n, 200 + R, 1.0)
+    a.view(np.uint32)[::97] = 0x7F800001          # NaNs, a tie and a subnormal sprinkled in
+    b.view(np.uint32)[5::89] = 0x3F808000
+    b.view(np.uint32)[7::101] = 0x00018000
+    p = Pair(n, chunk, R, mode)
+    outs = [zeros(n * p.esize) for _ in range(2)]
+    p.run(up(a), up(b), outs)
+    want = _want(a, b, mode)
+    dt = np.uint32 if mode == x.OUT_F32 else np.uint16
+    assert np.array_equal(down(outs[0], dt), want)
+    assert np.array_equal(down(outs[1], dt), want)
+
+
+@pytest.mark.parametrize("delays", [("w0",), ("w1",), ("c0",), ("c1",), ("c1", "w0"), ("c0", "w1"),
+                                    ("w0", "w1")])
+def test_delayed_streams_two_slots(delays):
+    """One slow stream at a time (or two): a missing wait would let a slot be
+    overwritten before its reader ran, or read before its writer."""
+    n, chunk, R = 40 * 256 + 17, 512, 2          # 41 chunks of 256 elements
+    a = dg.normal_f32(n, 7, 0.5)
+    b = dg.normal_f32(n, 8, 0.5)
+    p = Pair(n, chunk, R, x.OUT_F32)
+    outs = [zeros(n * 4) for _ in range(2)]
+    say("streamed delays", delays)
+    p.run(up(a), up(b), outs, delays)
+    want = _want(a, b, x.OUT_F32)
+    assert np.array_equal(down(outs[0], np.uint32), want)
+    assert np.array_equal(down(outs[1], np.uint32), want)
+
+
+def test_back_to_back_calls_reuse_rings_and_events():
+    n, chunk, R = 20 * 128 + 3, 256, 2
+    p = Pair(n, chunk, R, x.OUT_BF16)
+    inputs = [(dg.normal_f32(n, 30 + k, 1.0), dg.normal_f32(n, 40 + k, 1.0)) for k in range(3)]
+    outs = [[zeros(n * 2) for _ in range(2)] for _ in range(3)]
+    dev_in = [(up(a), up(b)) for a, b in inputs]
+    torch.cuda.synchronize()
+    for k, (da, db) in enumerate(dev_in):
+        # a slow wire stream before the second call, a slow compute stream before the third
+        p.run(da, db, outs[k], delays=[(), ("w1",), ("c0",)][k])
+    torch.cuda.synchronize()
+    for k, (a, b) in enumerate(inputs):
+        want = _want(a, b, x.OUT_BF16)
+        assert np.array_equal(down(outs[k][0], np.uint16), want), k
+        assert np.array_equal(down(outs[k][1], np.uint16), want), k
+
+
+def test_prompt_batch_2048x5120_two_512k_slots():
+    n = 2048 * 5120
+    a = dg.prompt_partial(n, dg.seed_for(2, 0, 2048))
+    b = dg.prompt_partial(n, dg.seed_for(2, 1, 2048))
+    p = Pair(n, 512 * 1024, 2, x.OUT_F32)
+    outs = [zeros(n * 4) for _ in range(2)]
+    say("streamed 2048 x 5120")
+    p.run(up(a), up(b), outs)
+    want = _want(a, b, x.OUT_F32)
+    assert np.array_equal(down(outs[0], np.uint32), want)
+    assert np.array_equal(down(outs[1], np.uint32), want)

@@ -1,0 +1,145 @@
+"""Hazard analysis of the streamed two-rank all-reduce schedule, on the CPU.
+
+The copy-engine page's review traced every read-after-write and
+write-after-read hazard across its streams by hand; here the library's own
+operation list (xfer_allreduce2_schedule) is checked mechanically: build the
+happens-before relation from stream order and event waits, then require every
+pair of operations that touch the same slot, at least one of them writing, to
+be ordered the way they were issued.  Removing a wait that carries a
+read-after-write dependency must expose a hazard, and with one slot (R = 1)
+every wait is needed.
+"""
+import itertools
+
+import pytest
+
+import bf16_wire_all_amd as x
+
+
+def _accesses(op):
+    """(buffer, is_write) pairs of one operation; buffers are (name, rank, slot)."""
+    r, s = op["rank"], op["slot"]
+    if op["kind"] == x.OP_PACK:
+        return [(("send", r, s), True)]
+    if op["kind"] == x.OP_WIRE:
+        return [(("send", r, s), False), (("recv", 1 - r, s), True)]
+    return [(("send", r, s), False), (("recv", r, s), False), (("out", r, op["chunk"]), True)]
+
+
+def _happens_before(ops):
+    """hb[i] = set of ops that happen before op i (transitively)."""
+    n = len(ops)
+    preds = [set() for _ in range(n)]
+    last_on_stream = {}
+    last_record = {}
+    for i, op in enumerate(ops):
+        if op["stream"] in last_on_stream:
+            preds[i].add(last_on_stream[op["stream"]])
+        for e in op["waits"]:
+            if e in last_record:          # a wait on an event not recorded in this call is a no-op
+                preds[i].add(last_record[e])
+        last_on_stream[op["stream"]] = i
+        last_record[op["record"]] = i
+    hb = []
+    for i in range(n):
+        s = set()
+        for p in preds[i]:
+            s.add(p)
+            s |= hb[p]
+        hb.append(s)
+    return hb
+
+
+def _hazards(ops):
+    hb = _happens_before(ops)
+    acc = [_accesses(o) for o in ops]
+    bad = []
+    for j in range(len(ops)):
+        for i in range(j):
+            for (bi, wi), (bj, wj) in itertools.product(acc[i], acc[j]):
+                if bi == bj and (wi or wj) and i not in hb[j]:
+                    bad.append((i, j, bi))
+    return bad
+
+
+def _without_wait(ops, idx, event):
+    out = [dict(o, waits=list(o["waits"])) for o in ops]
+    out[idx]["waits"].remove(event)
+    return out
+
+
+@pytest.mark.parametrize("R", [1, 2, 3, 4])
+@pytest.mark.parametrize("n_chunks", [1, 2, 3, 5, 9])
+def test_schedule_has_no_unordered_conflicts(R, n_chunks):
+    ops = x.allreduce2_schedule(n_chunks, R)
+    assert len(ops) == 6 * n_chunks
+    assert _hazards(ops) == []
+
+
+@pytest.mark.parametrize("R", [1, 2, 3])
+def test_read_after_write_waits_are_load_bearing(R):
+    """Dropping the wire copy's wait for its packed chunk, or the combine's
+    wait for the peer's copy, lets a read overtake its write."""
+    ops = x.allreduce2_schedule(2 * R + 1, R)
+    for idx, op in enumerate(ops):
+        if op["kind"] == x.OP_WIRE:
+            e = x.allreduce2_event_id(x.EV_PACKED, op["rank"], op["slot"], R)
+        elif op["kind"] == x.OP_COMBINE:
+            e = x.allreduce2_event_id(x.EV_SENT, 1 - op["rank"], op["slot"], R)
+        else:
+            continue
+        assert _hazards(_without_wait(ops, idx, e)), (idx, op)
+
+
+def test_with_one_slot_every_wait_is_needed():
+    R = 1
+    ops = x.allreduce2_schedule(4, R)
+    recorded = set()
+    checked = 0
+    for idx, op in enumerate(ops):
+        for e in op["waits"]:
+            if e in recorded:                 # waits that create an edge within the call
+                assert _hazards(_without_wait(ops, idx, e)), (idx, op, e)
+                checked += 1
+        recorded.add(op["record"])
+    assert checked >= 15
+
+
+def test_schedule_shape_and_events():
+    R = 2
+    ops = x.allreduce2_schedule(3, R)
+    kinds = [(o["kind"], o["rank"]) for o in ops[:6]]
+    assert kinds == [(0, 0), (0, 1), (1, 0), (1, 1), (2, 0), (2, 1)]
+    assert {o["stream"] for o in ops if o["kind"] == x.OP_WIRE} == {2, 3}
+    ids = {x.allreduce2_event_id(k, r, s, R) for k in range(3) for r in range(2) for s in range(R)}
+    assert ids == set(range(6 * R))
+    with pytest.raises(x.XferError):
+        x.allreduce2_schedule(3, 0)
+
+
+def test_streamed_argument_checks():
+    """Refusals that happen before any runtime call (no GPU needed)."""
+    d = x.AllReduce2Desc()
+    base = 0x10000000
+    for r in range(2):
+        d.src[r] = base + r * 0x100000
+        d.send[r] = base + 0x400000 + r * 0x10000
+        d.recv[r] = base + 0x500000 + r * 0x10000
+        d.out[r] = base + 0x600000 + r * 0x100000
+    d.n, d.chunk_bytes, d.ring_bytes, d.out_mode = 1000, 64, 128, 0
+    d.events = 0x1234
+    L = x.lib()
+    import ctypes
+    for field, value in (("out_mode", 5), ("chunk_bytes", 24), ("ring_bytes", 96)):
+        bad = x.AllReduce2Desc.from_buffer_copy(d)
+        setattr(bad, field, value)
+        assert L.xfer_allreduce2_streamed(ctypes.byref(bad)) == x.E_INVAL
+    bad = x.AllReduce2Desc.from_buffer_copy(d)
+    bad.recv[1] = bad.send[0] + 64            # receive ring overlaps a send ring
+    assert L.xfer_allreduce2_streamed(ctypes.byref(bad)) == x.E_INVAL
+    bad = x.AllReduce2Desc.from_buffer_copy(d)
+    bad.out[0] = base + 8                     # misaligned and overlapping
+    assert L.xfer_allreduce2_streamed(ctypes.byref(bad)) == x.E_INVAL
+    empty = x.AllReduce2Desc.from_buffer_copy(d)
+    empty.n = 0
+    assert L.xfer_allreduce2_streamed(ctypes.byref(empty)) == x.OK
