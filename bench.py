@@ -83,7 +83,7 @@ class Workload:
     seeded random order, so every lane breaks into many runs (the greedy
     table, and a second table with one run per segment, are both gathered)."""
 
-    def __init__(self, dev, tokens=TOKENS, shuffled=False):
+    def __init__(self, dev, tokens=TOKENS, shuffled=False, n_blocks=N_BLOCKS, seg=SEG):
         import numpy as np
         import torch
 
@@ -92,6 +92,7 @@ class Workload:
 
         self.x, self.torch, self.np = x, torch, np
         self.tokens, self.shuffled = tokens, shuffled
+        self.n_blocks, self.seg = n_blocks, seg
         n = tokens * HIDDEN
         self.n = n
         self.n_chunks = -(-n // (CHUNK // 2))
@@ -115,30 +116,32 @@ class Workload:
         self.ws = torch.zeros(x.argmax_workspace_bytes(ROWS, SPLIT, VOCAB - SPLIT), dtype=torch.uint8, device=dev)
         self.top2 = torch.zeros(ROWS * 16, dtype=torch.uint8, device=dev)
 
-        rb = dg.region_bytes_for(N_BLOCKS, N_SLOTS, SEG)
+        B, SG = n_blocks, seg
+        rb = dg.region_bytes_for(B, N_SLOTS, SG)
         self.regions = [torch.empty(rb, dtype=torch.uint8, device=dev) for _ in range(2)]
         bases = [r.data_ptr() for r in self.regions]
-        pos = dg.permutation(N_BLOCKS, dg.seed_for(5, 0, 1)) if shuffled else None
-        self.src_addrs = dg.kv_src_addrs(N_BLOCKS, N_SLOTS, SEG, bases, pos=pos)
+        pos = dg.permutation(B, dg.seed_for(5, 0, 1)) if shuffled else None
+        self.src_addrs = dg.kv_src_addrs(B, N_SLOTS, SG, bases, pos=pos)
         self.region_hosts = []
         for i, r in enumerate(self.regions):
             h = np.empty(rb, np.uint8)
-            dg.fill_region(h, bases[i], self.src_addrs, SEG, dg.seed_for(4, 0, i))
+            dg.fill_region(h, bases[i], self.src_addrs, SG, dg.seed_for(4, 0, i))
             r.copy_(torch.from_numpy(h))
             self.region_hosts.append(h)
-        self.src_table = x.runs_encode(self.src_addrs, SEG)
+        self.src_table = x.runs_encode(self.src_addrs, SG)
         self.src_plan_buf = torch.zeros(x.runs_plan_bytes(self.src_table), dtype=torch.uint8, device=dev)
         self.src_plan = x.runs_prepare(self.src_table, [(b, rb) for b in bases], False, self.src_plan_buf)
         self.seg_plan = None
         if shuffled:
             # the unencoded worst case: one run per segment
-            self.seg_table = x.runs_encode(self.src_addrs, SEG, max_count=1)
+            self.seg_table = x.runs_encode(self.src_addrs, SG, max_count=1)
             self.seg_plan_buf = torch.zeros(x.runs_plan_bytes(self.seg_table), dtype=torch.uint8, device=dev)
             self.seg_plan = x.runs_prepare(self.seg_table, [(b, rb) for b in bases], False, self.seg_plan_buf)
-        self.staging = torch.empty(2 * N_SLOTS * N_BLOCKS * SEG, dtype=torch.uint8, device=dev)
-        self.dst = torch.full((N_BLOCKS * N_SLOTS * DST_SLOT_STRIDE,), 0xA5, dtype=torch.uint8, device=dev)
-        self.dst_addrs = dg.kv_dst_addrs(N_BLOCKS, N_SLOTS, SEG, self.dst.data_ptr(), DST_SLOT_STRIDE)
-        self.dst_table = x.runs_encode(self.dst_addrs, SEG)
+        self.staging = torch.empty(2 * N_SLOTS * B * SG, dtype=torch.uint8, device=dev)
+        slot_stride = 3 * SG  # K, V and a gap segment per slot
+        self.dst = torch.full((B * N_SLOTS * slot_stride,), 0xA5, dtype=torch.uint8, device=dev)
+        self.dst_addrs = dg.kv_dst_addrs(B, N_SLOTS, SG, self.dst.data_ptr(), slot_stride)
+        self.dst_table = x.runs_encode(self.dst_addrs, SG)
         self.dst_plan_buf = torch.zeros(x.runs_plan_bytes(self.dst_table), dtype=torch.uint8, device=dev)
         self.dst_plan = x.runs_prepare(self.dst_table, [(self.dst.data_ptr(), self.dst.numel())], True,
                                        self.dst_plan_buf)
@@ -164,7 +167,12 @@ class Workload:
         return ks
 
     def algorithmic_bytes(self):
-        return algorithmic_bytes(self.tokens, ("gather_per_segment",) if self.seg_plan is not None else ())
+        ab = algorithmic_bytes(self.tokens, ("gather_per_segment",) if self.seg_plan is not None else ())
+        kv = self.n_blocks * N_SLOTS * 2 * self.seg
+        for k in ("gather", "scatter", "gather_per_segment"):
+            if k in ab:
+                ab[k] = 2 * kv
+        return ab
 
 
 def run_gpu(steps, warmup, workload):
@@ -211,26 +219,26 @@ def cpu_baseline(w, budget_s=12.0):
     ring_b = np.ones(w.n_chunks * ce, np.uint16)
     regions = [(r.data_ptr(), h) for r, h in zip(w.regions, w.region_hosts)]
     src_t = oracle.RunTable(w.src_table.runs_per_lane, w.src_table.run_base, w.src_table.run_stride,
-                            w.src_table.run_count, N_BLOCKS)
+                            w.src_table.run_count, w.n_blocks)
     dst_t = oracle.RunTable(w.dst_table.runs_per_lane, w.dst_table.run_base, w.dst_table.run_stride,
-                            w.dst_table.run_count, N_BLOCKS)
-    staging = np.ones(2 * N_SLOTS * N_BLOCKS * SEG, np.uint8)
-    dst = np.full(N_BLOCKS * N_SLOTS * DST_SLOT_STRIDE, 0xA5, np.uint8)
+                            w.dst_table.run_count, w.n_blocks)
+    staging = np.ones(2 * N_SLOTS * w.n_blocks * w.seg, np.uint8)
+    dst = np.full(w.dst.numel(), 0xA5, np.uint8)
     dst_regions = [(w.dst.data_ptr(), dst)]
     step_bytes = sum(w.algorithmic_bytes().values())
     seg_t = None
     if w.seg_plan is not None:
         seg_t = oracle.RunTable(w.seg_table.runs_per_lane, w.seg_table.run_base, w.seg_table.run_stride,
-                                w.seg_table.run_count, N_BLOCKS)
+                                w.seg_table.run_count, w.n_blocks)
     reps, t_total = 0, 0.0
     while t_total < budget_s and reps < 50:
         t0 = time.perf_counter()
         oracle.pack(w.a_host, ring_a.size, ce, 0, w.n_chunks, ring=ring_a)
         oracle.pack(w.b_host, ring_b.size, ce, 0, w.n_chunks, ring=ring_b)
-        oracle.gather(src_t, SEG, regions, staging=staging)
+        oracle.gather(src_t, w.seg, regions, staging=staging)
         if seg_t is not None:
-            oracle.gather(seg_t, SEG, regions, staging=staging)
-        oracle.scatter(dst_t, SEG, dst_regions, staging)
+            oracle.gather(seg_t, w.seg, regions, staging=staging)
+        oracle.scatter(dst_t, w.seg, dst_regions, staging)
         oracle.argmax_merge(w.logits_host, SPLIT, 1)
         oracle.combine2(ring_a[:n], ring_b[:n], 0)
         t_total += time.perf_counter() - t0
@@ -259,6 +267,12 @@ WORKLOADS = {
                     "(16x129280), gather of 1000 x 288 x 2 x 4 KiB with a shuffled block order by the greedy "
                     "run table (288,000 runs) and by one run per segment (576,000 runs), scatter",
         "roofline_kernel": ("gather", "gather_runs (shuffled blocks, 288,000 runs)", "gather_fragmented"),
+    },
+    "segments64k": {
+        "args": {"tokens": TOKENS, "shuffled": False, "n_blocks": 200, "seg": 65536},
+        "describe": "64 KiB segments: gather+scatter of 200 blocks x 288 slots x 2 x 64 KiB by run table (576 "
+                    "runs, 7200 MiB per set), with the 2048x5120 pack/combine and the 16x129280 argmax",
+        "roofline_kernel": ("gather", "gather_runs (64 KiB segments, 576 runs)", "gather_64k"),
     },
 }
 

@@ -14,7 +14,7 @@ namespace {
 using xfer::PlanView;
 
 constexpr uint32_t kPlanMagic = 0x584E5552u;  // "RUNX"
-constexpr uint32_t kDefaultTileBlocks = 2;    // blocks per gather/scatter workgroup
+constexpr uint64_t kTileBytes = 8192;         // segment bytes per gather/scatter workgroup (target)
 constexpr uint32_t kDefaultGroupBlocks = 32;  // blocks per run-index entry
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
@@ -45,7 +45,7 @@ bool run_addr(uint64_t base, int64_t stride, uint64_t k, uint64_t *out) {
 
 // Byte layout of a plan inside its device buffer.
 struct Layout {
-  uint32_t tile_blocks, n_tiles, group_blocks, n_groups;
+  uint32_t tile_blocks, n_tiles, group_blocks, n_groups, pieces;
   uint64_t off_group_run, off_run_start, off_run_base, off_run_stride, total;
 };
 
@@ -53,7 +53,16 @@ uint64_t up16(uint64_t x) { return (x + 15u) & ~15ull; }
 
 Layout layout_for(const xfer_run_table *t) {
   Layout L{};
-  L.tile_blocks = kDefaultTileBlocks;
+  // Work per workgroup: about kTileBytes.  Small segments: a power-of-two
+  // number of blocks (it must divide the group size), e.g. 2 blocks of 4 KiB.
+  // Large segments whose vector count is a power of two: one block, split
+  // into kTileBytes pieces, one workgroup each (8 pieces of a 64 KiB segment).
+  uint32_t tb = 1;
+  while (tb * 2 <= xfer::kMaxTileBlocks && (uint64_t)tb * 2 * t->seg_bytes <= kTileBytes) tb *= 2;
+  L.tile_blocks = tb;
+  const uint64_t vps = t->seg_bytes / 16;
+  L.pieces = 1;
+  if (t->seg_bytes > kTileBytes && (vps & (vps - 1)) == 0) L.pieces = (uint32_t)(t->seg_bytes / kTileBytes);
   L.group_blocks = kDefaultGroupBlocks;
   L.n_tiles = (t->n_blocks + L.tile_blocks - 1) / L.tile_blocks;
   L.n_groups = (t->n_blocks + L.group_blocks - 1) / L.group_blocks;
@@ -141,6 +150,7 @@ bool plan_ok(const xfer_runs_plan *p) {
   if (p->tile_blocks == 0 || p->tile_blocks > xfer::kMaxTileBlocks) return false;
   if (p->group_blocks == 0 || p->group_blocks > xfer::kMaxGroupBlocks || p->group_blocks % p->tile_blocks)
     return false;
+  if (p->pieces == 0 || (p->seg_bytes / 16) % p->pieces || (p->pieces > 1 && p->tile_blocks != 1)) return false;
   if (p->off_run_stride + up16(p->n_runs * 8) > p->dev_bytes) return false;
   return true;
 }
@@ -160,8 +170,10 @@ PlanView view_of(const xfer_runs_plan *p) {
   v.n_groups = p->n_groups;
   v.seg_bytes = p->seg_bytes;
   v.vps = (uint32_t)(p->seg_bytes / 16);
-  v.vps_log2 = 32;
-  if ((v.vps & (v.vps - 1)) == 0) v.vps_log2 = (uint32_t)__builtin_ctz(v.vps);
+  v.pieces = p->pieces;
+  v.piece_vecs = v.vps / p->pieces;
+  v.piece_log2 = 32;
+  if ((v.piece_vecs & (v.piece_vecs - 1)) == 0) v.piece_log2 = (uint32_t)__builtin_ctz(v.piece_vecs);
   return v;
 }
 
@@ -388,6 +400,7 @@ int xfer_runs_prepare(const xfer_run_table *t, const xfer_region *regions, int n
   p.n_tiles = L.n_tiles;
   p.group_blocks = L.group_blocks;
   p.n_groups = L.n_groups;
+  p.pieces = L.pieces;
   p.magic = kPlanMagic;
   p.off_group_run = L.off_group_run;
   p.off_run_start = L.off_run_start;
@@ -403,7 +416,7 @@ int xfer_gather_runs(const xfer_runs_plan *plan, void *staging, size_t staging_b
   if (!plan_ok(plan)) return XFER_E_INVAL;
   const int st = staging_check(plan, (uintptr_t)staging, staging_bytes);
   if (st != XFER_OK) return st;
-  if ((uint64_t)plan->n_lanes * plan->n_tiles > (uint64_t)INT32_MAX) return XFER_E_UNSUPPORTED;
+  if ((uint64_t)plan->n_lanes * plan->n_tiles * plan->pieces > (uint64_t)INT32_MAX) return XFER_E_UNSUPPORTED;
   if (xfer::launch_gather(view_of(plan), staging, stream) != hipSuccess) return XFER_E_DEVICE;
   return XFER_OK;
 }
@@ -414,7 +427,7 @@ int xfer_scatter_runs(const void *staging, size_t staging_bytes, const xfer_runs
   if (!plan_ok(plan)) return XFER_E_INVAL;
   const int st = staging_check(plan, (uintptr_t)staging, staging_bytes);
   if (st != XFER_OK) return st;
-  if ((uint64_t)plan->n_lanes * plan->n_tiles > (uint64_t)INT32_MAX) return XFER_E_UNSUPPORTED;
+  if ((uint64_t)plan->n_lanes * plan->n_tiles * plan->pieces > (uint64_t)INT32_MAX) return XFER_E_UNSUPPORTED;
   if (xfer::launch_scatter(view_of(plan), staging, stream) != hipSuccess) return XFER_E_DEVICE;
   return XFER_OK;
 }

@@ -53,7 +53,9 @@ struct PlanView {
   uint32_t n_groups;          // per lane
   uint64_t seg_bytes;
   uint32_t vps;               // 16-byte vectors per segment, <= kMaxSegVectors
-  uint32_t vps_log2;          // log2(vps) if vps is a power of two, else 32
+  uint32_t pieces;            // workgroups per segment (1, or vps / piece_vecs)
+  uint32_t piece_vecs;        // vectors one workgroup copies per segment
+  uint32_t piece_log2;        // log2(piece_vecs) if a power of two, else 32
 };
 constexpr uint32_t kMaxGroupBlocks = 32;
 constexpr uint32_t kMaxTileBlocks = 32;

@@ -40,18 +40,18 @@ __device__ __forceinline__ void store16(uint64_t a, v4u v) {
   __builtin_nontemporal_store(v, reinterpret_cast<g_v4u *>(a));
 }
 
-// Vector v of the tile (v < nb * vps) is vector v mod vps of the tile's
-// segment v / vps.  Segments hold at most 2^16 vectors (host check), so all
-// tile-local indices fit 32 bits; POW2 replaces the division by a shift.
+// Vector v of the workgroup's share (v < nb * w, w = piece_vecs) is vector
+// v0 + v mod w of the tile's segment v / w.  Segments hold at most 2^16
+// vectors (host check), so all tile-local indices fit 32 bits; POW2 replaces
+// the division by a shift.
 template <bool POW2>
-__device__ __forceinline__ void split_index(uint32_t v, uint32_t vps, uint32_t vps_log2, uint32_t &j,
-                                            uint32_t &o) {
+__device__ __forceinline__ void split_index(uint32_t v, uint32_t w, uint32_t w_log2, uint32_t &j, uint32_t &o) {
   if (POW2) {
-    j = v >> vps_log2;
-    o = v & (vps - 1);
+    j = v >> w_log2;
+    o = v & (w - 1);
   } else {
-    j = v / vps;
-    o = v - j * vps;
+    j = v / w;
+    o = v - j * w;
   }
 }
 
@@ -63,8 +63,12 @@ __global__ __launch_bounds__(kThreads) void runs_copy_kernel(PlanView p, uint8_t
   __shared__ int64_t s_stride[kMaxGroupBlocks + 1];
   __shared__ uint64_t s_addr[kMaxTileBlocks];
 
-  const uint32_t l = blockIdx.x % p.n_lanes;
-  const uint32_t t = blockIdx.x / p.n_lanes;
+  // Workgroup -> (piece, lane, tile), pieces fastest: consecutive workgroups
+  // stream consecutive pieces of one segment, then the next lane's.
+  const uint32_t piece = blockIdx.x % p.pieces;
+  const uint32_t rest = blockIdx.x / p.pieces;
+  const uint32_t l = rest % p.n_lanes;
+  const uint32_t t = rest / p.n_lanes;
   const uint32_t b0 = t * p.tile_blocks;
   const uint32_t nb = min(p.tile_blocks, p.n_blocks - b0);
   const uint32_t tid = threadIdx.x;
@@ -98,22 +102,23 @@ __global__ __launch_bounds__(kThreads) void runs_copy_kernel(PlanView p, uint8_t
   }
   __syncthreads();
 
-  const uint32_t vps = p.vps;
-  const uint32_t total = nb * vps;
+  const uint32_t w = p.piece_vecs;
+  const uint64_t v0 = (uint64_t)piece * w;  // first vector of this workgroup's piece
+  const uint32_t total = nb * w;
   const uint64_t block_step = (uint64_t)p.n_lanes * p.seg_bytes;  // staging bytes between blocks
   const uint8_t *stage0 = (GATHER ? (const uint8_t *)staging_w : staging_r) +
                           ((uint64_t)b0 * p.n_lanes + l) * p.seg_bytes;
 
-  // Address of vector v on the read side (from) and on the write side.
+  // Address of vector v on the staging side and on the table side.
   auto stage_at = [&](uint32_t vv) {
     uint32_t j, o;
-    split_index<POW2>(vv, vps, p.vps_log2, j, o);
-    return (uint64_t)stage0 + j * block_step + 16ull * o;
+    split_index<POW2>(vv, w, p.piece_log2, j, o);
+    return (uint64_t)stage0 + j * block_step + 16ull * (v0 + o);
   };
   auto table_at = [&](uint32_t vv) {
     uint32_t j, o;
-    split_index<POW2>(vv, vps, p.vps_log2, j, o);
-    return s_addr[j] + 16ull * o;
+    split_index<POW2>(vv, w, p.piece_log2, j, o);
+    return s_addr[j] + 16ull * (v0 + o);
   };
   uint32_t v = tid;
   for (; v + (kUnroll - 1) * kThreads < total; v += kUnroll * kThreads) {
@@ -135,17 +140,17 @@ __global__ __launch_bounds__(kThreads) void runs_copy_kernel(PlanView p, uint8_t
 }  // namespace
 
 hipError_t launch_gather(const PlanView &p, void *staging, hipStream_t stream) {
-  const dim3 grid(p.n_lanes * p.n_tiles);
+  const dim3 grid(p.n_lanes * p.n_tiles * p.pieces);
   uint8_t *w = reinterpret_cast<uint8_t *>(staging);
-  if (p.vps_log2 < 32)
+  if (p.piece_log2 < 32)
     return launch(runs_copy_kernel<true, true>, grid, dim3(kThreads), 0, stream, p, w, (const uint8_t *)w);
   return launch(runs_copy_kernel<true, false>, grid, dim3(kThreads), 0, stream, p, w, (const uint8_t *)w);
 }
 
 hipError_t launch_scatter(const PlanView &p, const void *staging, hipStream_t stream) {
-  const dim3 grid(p.n_lanes * p.n_tiles);
+  const dim3 grid(p.n_lanes * p.n_tiles * p.pieces);
   const uint8_t *r = reinterpret_cast<const uint8_t *>(staging);
-  if (p.vps_log2 < 32)
+  if (p.piece_log2 < 32)
     return launch(runs_copy_kernel<false, true>, grid, dim3(kThreads), 0, stream, p, (uint8_t *)nullptr, r);
   return launch(runs_copy_kernel<false, false>, grid, dim3(kThreads), 0, stream, p, (uint8_t *)nullptr, r);
 }

@@ -183,6 +183,41 @@ def test_full_size_kv_gather_scatter(layout):
     torch.cuda.empty_cache()
 
 
+def test_full_size_64k_segments():
+    """200 blocks x 288 slots x 2 segments of 64 KiB (7200 MiB per set), dense,
+    and its scatter into a slot-major destination with a gap segment per slot."""
+    B, S, SEG = 200, dg.N_SLOTS, 65536
+    L = 2 * S
+    say("64 KiB segments regions")
+    regs, hosts, addrs = _world(B, S, SEG, None)
+    regions = [(r.data_ptr(), r.numel()) for r in regs]
+    oregions = [(r.data_ptr(), h) for r, h in zip(regs, hosts)]
+    t = x.runs_encode(addrs, SEG)
+    assert t.n_runs == L
+    say("64 KiB oracle gather")
+    want = oracle.gather(_otable(t), SEG, oregions)
+    staging = zeros(L * B * SEG)
+    plan, _buf = _plan(t, regions, False)
+    say("64 KiB gpu gather")
+    x.gather_runs(plan, staging)
+    got = down(staging)
+    assert np.array_equal(got, want)
+    del got, regs, hosts
+    torch.cuda.empty_cache()
+    dst = filled(B * S * 3 * SEG, 0xA5)
+    daddrs = dg.kv_dst_addrs(B, S, SEG, dst.data_ptr(), 3 * SEG)
+    dt = x.runs_encode(daddrs, SEG)
+    dwant = np.full(dst.numel(), 0xA5, np.uint8)
+    say("64 KiB oracle scatter")
+    oracle.scatter(_otable(dt), SEG, [(dst.data_ptr(), dwant)], want)
+    dplan, _dbuf = _plan(dt, [(dst.data_ptr(), dst.numel())], True)
+    say("64 KiB gpu scatter")
+    x.scatter_runs(staging, dplan)
+    assert np.array_equal(down(dst), dwant)
+    del dst, staging
+    torch.cuda.empty_cache()
+
+
 def test_plan_misuse_refused():
     regs, hosts, addrs = _world(4, 2, 64, None, n_regions=1)
     t = x.runs_encode(addrs, 64)
