@@ -83,7 +83,7 @@ class Workload:
     seeded random order, so every lane breaks into many runs (the greedy
     table, and a second table with one run per segment, are both gathered)."""
 
-    def __init__(self, dev, tokens=TOKENS, shuffled=False, n_blocks=N_BLOCKS, seg=SEG):
+    def __init__(self, dev, tokens=TOKENS, shuffled=False, n_blocks=N_BLOCKS, seg=SEG, coalesced=False):
         import numpy as np
         import torch
 
@@ -138,6 +138,16 @@ class Workload:
             self.seg_plan_buf = torch.zeros(x.runs_plan_bytes(self.seg_table), dtype=torch.uint8, device=dev)
             self.seg_plan = x.runs_prepare(self.seg_table, [(b, rb) for b in bases], False, self.seg_plan_buf)
         self.staging = torch.empty(2 * N_SLOTS * B * SG, dtype=torch.uint8, device=dev)
+        self.fetch_plan = None
+        if coalesced:
+            # the whole source set read by dense-group descriptors into one slab
+            self.groups = x.groups_plan(self.src_table, [(b, rb) for b in bases])
+            self.desc_buf = torch.zeros(max(16, x.descs_plan_bytes(len(self.groups.descs))), dtype=torch.uint8,
+                                        device=dev)
+            self.fetch_plan = x.descs_prepare(self.groups.descs, self.groups.slab_bytes,
+                                              [(b, rb) for b in bases], self.desc_buf)
+            self.slab = torch.empty(self.groups.slab_bytes, dtype=torch.uint8, device=dev)
+            log(f"bench: coalesced fetch with {len(self.groups.descs)} descriptors")
         slot_stride = 3 * SG  # K, V and a gap segment per slot
         self.dst = torch.full((B * N_SLOTS * slot_stride,), 0xA5, dtype=torch.uint8, device=dev)
         self.dst_addrs = dg.kv_dst_addrs(B, N_SLOTS, SG, self.dst.data_ptr(), slot_stride)
@@ -159,6 +169,8 @@ class Workload:
         ]
         if self.seg_plan is not None:
             ks.append(("gather_per_segment", lambda: x.gather_runs(self.seg_plan, self.staging)))
+        if self.fetch_plan is not None:
+            ks.append(("fetch_coalesced", lambda: x.copy_descs(self.fetch_plan, self.slab)))
         ks += [
             ("scatter", lambda: x.scatter_runs(self.staging, self.dst_plan)),
             ("argmax_top2", lambda: x.argmax_merge(self.s0, self.s1, x.TOP2, self.top2, self.ws)),
@@ -167,9 +179,11 @@ class Workload:
         return ks
 
     def algorithmic_bytes(self):
-        ab = algorithmic_bytes(self.tokens, ("gather_per_segment",) if self.seg_plan is not None else ())
+        extra = (("gather_per_segment",) if self.seg_plan is not None else ()) + \
+            (("fetch_coalesced",) if self.fetch_plan is not None else ())
+        ab = algorithmic_bytes(self.tokens, extra)
         kv = self.n_blocks * N_SLOTS * 2 * self.seg
-        for k in ("gather", "scatter", "gather_per_segment"):
+        for k in ("gather", "scatter", "gather_per_segment", "fetch_coalesced"):
             if k in ab:
                 ab[k] = 2 * kv
         return ab
@@ -259,20 +273,28 @@ WORKLOADS = {
         "describe": "transfer hot path: pack x2 + combine2 (2048x5120 F32 partials, 512 KiB BF16 chunks), "
                     "argmax merge (16x129280 BF16, split at 64768, top2), gather+scatter by run table "
                     "(1000 blocks x 288 slots x 2 x 4 KiB, one run per lane)",
-        "roofline_kernel": ("gather", "gather_runs (paged K/V, 576 runs)", "gather_dense"),
+        "roofline_kernel": ("gather", "gather_runs (paged K/V, 576 runs)", "runs_copy.hip", "gather_dense"),
     },
     "fragmented": {
         "args": {"tokens": 16384, "shuffled": True},
         "describe": "fragmented transfer: pack x2 + combine2 (16384x5120 F32 partials), argmax merge "
                     "(16x129280), gather of 1000 x 288 x 2 x 4 KiB with a shuffled block order by the greedy "
                     "run table (288,000 runs) and by one run per segment (576,000 runs), scatter",
-        "roofline_kernel": ("gather", "gather_runs (shuffled blocks, 288,000 runs)", "gather_fragmented"),
+        "roofline_kernel": ("gather", "gather_runs (shuffled blocks, 288,000 runs)", "runs_copy.hip",
+                            "gather_fragmented"),
     },
     "segments64k": {
         "args": {"tokens": TOKENS, "shuffled": False, "n_blocks": 200, "seg": 65536},
         "describe": "64 KiB segments: gather+scatter of 200 blocks x 288 slots x 2 x 64 KiB by run table (576 "
                     "runs, 7200 MiB per set), with the 2048x5120 pack/combine and the 16x129280 argmax",
-        "roofline_kernel": ("gather", "gather_runs (64 KiB segments, 576 runs)", "gather_64k"),
+        "roofline_kernel": ("gather", "gather_runs (64 KiB segments, 576 runs)", "runs_copy.hip", "gather_64k"),
+    },
+    "coalesced": {
+        "args": {"tokens": TOKENS, "shuffled": False, "coalesced": True},
+        "describe": "coalesced fetch: the step's kernels plus a read of the whole 1000 x 288 x 2 x 4 KiB source "
+                    "set by 72 dense-group descriptors (at most 32 MiB each) into one slab",
+        "roofline_kernel": ("fetch_coalesced", "copy_descs (72 dense-group reads)", "descs_copy.hip",
+                            "fetch_dense"),
     },
 }
 
@@ -322,11 +344,11 @@ def main():
         gbs = ab[name] / (ms * 1e-3) / 1e9
         kernels[name] = {"us": round(ms * 1e3, 2), "bytes": ab[name], "GBps": round(gbs, 1),
                          "frac_of_peak": round(gbs / PEAK_HBM_GBS, 4)}
-    rk, rk_label, rk_key = wl["roofline_kernel"]
+    rk, rk_label, rk_file, rk_key = wl["roofline_kernel"]
     g_gbs = ab[rk] / (kms[rk] * 1e-3) / 1e9
     roofline = {"kernel": rk_label, "bound": "hbm", "achieved": round(g_gbs, 1),
                 "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(g_gbs / PEAK_HBM_GBS, 4),
-                "traffic": measured_traffic("runs_copy.hip", rk_key)}
+                "traffic": measured_traffic(rk_file, rk_key)}
     line = {
         "metric": "achieved HBM GB/s (and % of peak) for pack+combine and run-table segment gather",
         "value": round(value, 1),

@@ -28,6 +28,7 @@ EXPORTED = [
     "xfer_argmax_merge", "xfer_runs_encode", "xfer_runs_validate", "xfer_runs_plan_bytes",
     "xfer_runs_prepare", "xfer_gather_runs", "xfer_scatter_runs", "xfer_allreduce2_event_id",
     "xfer_allreduce2_schedule", "xfer_events_create", "xfer_events_destroy", "xfer_allreduce2_streamed",
+    "xfer_groups_plan", "xfer_descs_plan_bytes", "xfer_descs_prepare", "xfer_copy_descs",
 ]
 
 
@@ -59,6 +60,13 @@ class AllReduce2Desc(ctypes.Structure):
                 ("out", ctypes.c_void_p * 2), ("n", ctypes.c_size_t), ("chunk_bytes", ctypes.c_size_t),
                 ("ring_bytes", ctypes.c_size_t), ("out_mode", ctypes.c_int), ("compute", ctypes.c_void_p * 2),
                 ("wire", ctypes.c_void_p * 2), ("events", ctypes.c_void_p)]
+
+
+class DescsPlan(ctypes.Structure):
+    _fields_ = [("dev", ctypes.c_void_p), ("dev_bytes", ctypes.c_uint64), ("n_descs", ctypes.c_uint64),
+                ("slab_bytes", ctypes.c_uint64), ("src_lo", ctypes.c_uint64), ("src_hi", ctypes.c_uint64),
+                ("max_pieces", ctypes.c_uint32), ("piece_bytes", ctypes.c_uint32), ("magic", ctypes.c_uint32),
+                ("reserved", ctypes.c_uint32)]
 
 
 class Region(ctypes.Structure):
@@ -119,6 +127,16 @@ def lib():
         L.xfer_events_destroy.restype = I
         L.xfer_allreduce2_streamed.argtypes = [ctypes.POINTER(AllReduce2Desc)]
         L.xfer_allreduce2_streamed.restype = I
+        L.xfer_groups_plan.argtypes = [ctypes.POINTER(RunTableC), ctypes.POINTER(Region), I, U64, P, U64,
+                                       ctypes.POINTER(U64), ctypes.POINTER(U64), P, P, ctypes.POINTER(U64),
+                                       ctypes.POINTER(U64)]
+        L.xfer_groups_plan.restype = I
+        L.xfer_descs_plan_bytes.argtypes = [U64]
+        L.xfer_descs_plan_bytes.restype = S
+        L.xfer_descs_prepare.argtypes = [P, U64, U64, ctypes.POINTER(Region), I, P, S, ctypes.POINTER(DescsPlan)]
+        L.xfer_descs_prepare.restype = I
+        L.xfer_copy_descs.argtypes = [ctypes.POINTER(DescsPlan), P, S, P]
+        L.xfer_copy_descs.restype = I
         _lib = L
     return _lib
 
@@ -365,3 +383,78 @@ def allreduce2_streamed(src, send, recv, out, chunk_bytes: int, mode: int, compu
     d.out_mode = mode
     d.events = ctypes.cast(events.array, ctypes.c_void_p)
     return lib().xfer_allreduce2_streamed(ctypes.byref(d))
+
+
+# ---------------------------------------------- coalesced fetch by dense group
+
+DESC = np.dtype([("src", "<u8"), ("dst_off", "<u8"), ("bytes", "<u8")])
+MAX_READ_BYTES = 32 << 20
+
+
+@dataclass
+class GroupsPlan:
+    descs: np.ndarray          # DESC[n]
+    slab_bytes: int
+    local_base: np.ndarray     # uint64[n_runs], slab offsets
+    local_stride: np.ndarray   # int64[n_runs]
+    n_groups: int
+    n_dense: int
+
+    def local_table(self, t: RunTable, slab_base: int) -> RunTable:
+        """The source table's runs re-based onto the slab at slab_base."""
+        return RunTable(t.runs_per_lane.copy(), (self.local_base + np.uint64(slab_base)).astype(np.uint64),
+                        self.local_stride.copy(), t.run_count.copy(), t.n_blocks, t.seg_bytes)
+
+
+def groups_plan_status(t: RunTable, regions, max_desc_bytes: int = MAX_READ_BYTES):
+    tc = t.c()
+    regs = _regions(regions)
+    n = ctypes.c_uint64(0)
+    slab = ctypes.c_uint64(0)
+    ng = ctypes.c_uint64(0)
+    nd = ctypes.c_uint64(0)
+    lb = np.zeros(max(1, t.n_runs), np.uint64)
+    ls = np.zeros(max(1, t.n_runs), np.int64)
+    st = lib().xfer_groups_plan(ctypes.byref(tc), regs, len(regions), max_desc_bytes, None, 0, ctypes.byref(n),
+                                ctypes.byref(slab), lb.ctypes.data, ls.ctypes.data, ctypes.byref(ng),
+                                ctypes.byref(nd))
+    if st not in (OK, E_RANGE):
+        return st, None
+    descs = np.zeros(max(1, n.value), DESC)
+    st = lib().xfer_groups_plan(ctypes.byref(tc), regs, len(regions), max_desc_bytes, descs.ctypes.data,
+                                n.value, ctypes.byref(n), ctypes.byref(slab), lb.ctypes.data, ls.ctypes.data,
+                                ctypes.byref(ng), ctypes.byref(nd))
+    if st != OK:
+        return st, None
+    return OK, GroupsPlan(descs[:n.value].copy(), slab.value, lb[:t.n_runs].copy(), ls[:t.n_runs].copy(),
+                          ng.value, nd.value)
+
+
+def groups_plan(t: RunTable, regions, max_desc_bytes: int = MAX_READ_BYTES) -> GroupsPlan:
+    """regions: list of (device base, bytes)."""
+    st, plan = groups_plan_status(t, regions, max_desc_bytes)
+    _check(st, "xfer_groups_plan")
+    return plan
+
+
+def descs_plan_bytes(n_descs: int) -> int:
+    return int(lib().xfer_descs_plan_bytes(n_descs))
+
+
+def descs_prepare_status(descs: np.ndarray, slab_bytes: int, regions, dev_ptr: int, dev_bytes: int):
+    d = np.ascontiguousarray(descs, dtype=DESC)
+    plan = DescsPlan()
+    st = lib().xfer_descs_prepare(d.ctypes.data if d.size else None, d.size, slab_bytes, _regions(regions),
+                                  len(regions), dev_ptr, dev_bytes, ctypes.byref(plan))
+    return st, plan
+
+
+def descs_prepare(descs: np.ndarray, slab_bytes: int, regions, dev) -> DescsPlan:
+    st, plan = descs_prepare_status(descs, slab_bytes, regions, _dev(dev), dev.numel() * dev.element_size())
+    _check(st, "xfer_descs_prepare")
+    return plan
+
+
+def copy_descs(plan: DescsPlan, slab, stream=None) -> None:
+    _check(lib().xfer_copy_descs(ctypes.byref(plan), _dev(slab), slab.numel() * slab.element_size(),
+                                 _stream(stream)), "xfer_copy_descs")

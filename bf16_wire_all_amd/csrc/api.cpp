@@ -27,8 +27,10 @@ bool overlaps(uintptr_t a, uint64_t na, uintptr_t b, uint64_t nb) {
 
 bool mul_ok(uint64_t a, uint64_t b, uint64_t *out) { return !__builtin_mul_overflow(a, b, out); }
 
+}  // namespace
+
 // base + k * stride, every step checked for 64-bit overflow.
-bool run_addr(uint64_t base, int64_t stride, uint64_t k, uint64_t *out) {
+bool xfer::run_addr(uint64_t base, int64_t stride, uint64_t k, uint64_t *out) {
   if (k > (uint64_t)INT64_MAX) return false;
   int64_t prod;
   if (__builtin_mul_overflow((int64_t)k, stride, &prod)) return false;
@@ -42,6 +44,9 @@ bool run_addr(uint64_t base, int64_t stride, uint64_t k, uint64_t *out) {
   }
   return true;
 }
+
+namespace {
+using xfer::run_addr;
 
 // Byte layout of a plan inside its device buffer.
 struct Layout {
@@ -74,10 +79,12 @@ Layout layout_for(const xfer_run_table *t) {
   return L;
 }
 
+}  // namespace
+
 // The checks of xfer_runs_validate; on success also reports the byte span
 // covering every segment.
-int validate(const xfer_run_table *t, const xfer_region *regions, int n_regions, int is_dst, uint64_t *span_lo,
-             uint64_t *span_hi) {
+int xfer::validate_table(const xfer_run_table *t, const xfer_region *regions, int n_regions, int is_dst,
+                         uint64_t *span_lo, uint64_t *span_hi) {
   if (!t) return XFER_E_INVAL;
   if (n_regions < 0 || (n_regions > 0 && !regions)) return XFER_E_INVAL;
   if (t->n_lanes > 0 && !t->runs_per_lane) return XFER_E_INVAL;
@@ -144,6 +151,9 @@ int validate(const xfer_run_table *t, const xfer_region *regions, int n_regions,
   if (span_hi) *span_hi = t->n_runs ? hi_all : 0;
   return XFER_OK;
 }
+
+namespace {
+using xfer::validate_table;
 
 bool plan_ok(const xfer_runs_plan *p) {
   if (!p || p->magic != kPlanMagic || !p->dev) return false;
@@ -342,7 +352,7 @@ int xfer_runs_encode(const uint64_t *addrs, uint32_t n_lanes, uint32_t n_blocks,
 }
 
 int xfer_runs_validate(const xfer_run_table *t, const xfer_region *regions, int n_regions, int is_dst) {
-  return validate(t, regions, n_regions, is_dst, nullptr, nullptr);
+  return validate_table(t, regions, n_regions, is_dst, nullptr, nullptr);
 }
 
 size_t xfer_runs_plan_bytes(const xfer_run_table *t) {
@@ -353,7 +363,7 @@ size_t xfer_runs_plan_bytes(const xfer_run_table *t) {
 int xfer_runs_prepare(const xfer_run_table *t, const xfer_region *regions, int n_regions, int is_dst, void *dev,
                       size_t dev_bytes, xfer_runs_plan *out) {
   uint64_t span_lo = 0, span_hi = 0;
-  const int st = validate(t, regions, n_regions, is_dst, &span_lo, &span_hi);
+  const int st = validate_table(t, regions, n_regions, is_dst, &span_lo, &span_hi);
   if (st != XFER_OK) return st;
   if (!out) return XFER_E_INVAL;
   const Layout L = layout_for(t);

@@ -22,6 +22,11 @@ static inline hipError_t launch(void (*kernel)(KArgs...), dim3 grid, dim3 block,
   return hipLaunchKernel((const void *)kernel, grid, block, argv, lds, stream);
 }
 
+// ---- host helpers shared by the entry points (api.cpp)
+int validate_table(const xfer_run_table *t, const xfer_region *regions, int n_regions, int is_dst,
+                   uint64_t *span_lo, uint64_t *span_hi);
+bool run_addr(uint64_t base, int64_t stride, uint64_t k, uint64_t *out);
+
 // ---- pack / combine (pack_combine.hip)
 hipError_t launch_pack(const float *src, uint64_t n_elems, uint16_t *ring, uint64_t ring_elems,
                        uint64_t slot0_elem, hipStream_t stream);
@@ -62,5 +67,10 @@ constexpr uint32_t kMaxTileBlocks = 32;
 constexpr uint32_t kMaxSegVectors = 1u << 16;  // 1 MiB segments
 hipError_t launch_gather(const PlanView &p, void *staging, hipStream_t stream);
 hipError_t launch_scatter(const PlanView &p, const void *staging, hipStream_t stream);
+
+// ---- descriptor copies (descs_copy.hip)
+constexpr uint32_t kDescPieceBytes = 8192;
+hipError_t launch_copy_descs(const xfer_desc *descs, uint64_t n_descs, uint32_t max_pieces, void *slab,
+                             hipStream_t stream);
 
 }  // namespace xfer

@@ -306,6 +306,82 @@ XFER_API int xfer_gather_runs(const xfer_runs_plan *src_plan, void *staging, siz
 XFER_API int xfer_scatter_runs(const void *staging, size_t staging_bytes, const xfer_runs_plan *dst_plan,
                       hipStream_t stream);
 
+/* ------------------------------------------ coalesced fetch by dense group */
+
+/* One contiguous copy: bytes from device address src to slab offset dst_off. */
+typedef struct {
+  uint64_t src;
+  uint64_t dst_off;
+  uint64_t bytes;
+} xfer_desc;
+
+/*
+ * xfer_groups_plan - the requester's planning of [RUNS] "What this PR does"
+ * steps 2-4 and "READ splitting", host only:
+ *   1. runs are bucketed by the region that holds them and sorted by base;
+ *   2. sweeping that order, a run joins the open group when it covers the
+ *      same blocks, has the same stride, starts where the group's per-block
+ *      chunk ends, and the grown chunk still fits the stride (|stride| >=
+ *      chunk, any chunk for one-block runs); otherwise it opens a new group;
+ *   3. a group whose per-block chunks are back to back (|stride| == chunk, or
+ *      one block) is dense: one contiguous range, mirrored into the slab as
+ *      is; any other group is read block by block into a dense local mirror;
+ *   4. every range is split into descriptors of at most max_desc_bytes
+ *      (32 MiB in [RUNS]).
+ * Groups are laid out in the slab in that order.  The rebuilt local address
+ * of every segment is arithmetic ([RUNS] step 5): local_base[r] and
+ * local_stride[r] give run r's segments as slab offsets
+ * (local = local_base[r] + i * local_stride[r]), so the table with these
+ * arrays addresses the slab.
+ *
+ *   t, regions     as xfer_runs_validate (source table); validated first.
+ *   descs          (host) capacity cap_descs; *n_descs receives the count.
+ *   slab_bytes     receives the slab size (the sum of the descriptor bytes).
+ *   local_base, local_stride  (host) n_runs each.
+ *   n_groups, n_dense  receive the group counts (may be NULL).
+ * Errors: those of xfer_runs_validate; XFER_E_INVAL for NULL outputs or a
+ * max_desc_bytes that is 0 or not a multiple of 16; XFER_E_RANGE if
+ * cap_descs is too small (then *n_descs holds the count needed; descs NULL
+ * with cap_descs 0 asks for the count only).
+ */
+XFER_API int xfer_groups_plan(const xfer_run_table *t, const xfer_region *regions, int n_regions,
+                              uint64_t max_desc_bytes, xfer_desc *descs, uint64_t cap_descs, uint64_t *n_descs,
+                              uint64_t *slab_bytes, uint64_t *local_base, int64_t *local_stride, uint64_t *n_groups,
+                              uint64_t *n_dense);
+
+/* A validated descriptor list in a caller-owned device buffer (plain data). */
+typedef struct {
+  void *dev;
+  uint64_t dev_bytes;
+  uint64_t n_descs;
+  uint64_t slab_bytes;
+  uint64_t src_lo, src_hi;  /* byte range covering every source range */
+  uint32_t max_pieces;      /* private from here on */
+  uint32_t piece_bytes;
+  uint32_t magic;
+  uint32_t reserved;
+} xfer_descs_plan;
+
+XFER_API size_t xfer_descs_plan_bytes(uint64_t n_descs);
+
+/*
+ * xfer_descs_prepare - check a descriptor list and upload it (blocking):
+ * every descriptor has bytes > 0 and src, dst_off, bytes multiples of 16,
+ * no source range wraps or leaves the declared regions (XFER_E_RANGE), the
+ * destination ranges lie in [0, slab_bytes) and are pairwise disjoint
+ * (XFER_E_OVERLAP).  dev: device, 16-byte aligned, xfer_descs_plan_bytes().
+ */
+XFER_API int xfer_descs_prepare(const xfer_desc *descs, uint64_t n_descs, uint64_t slab_bytes,
+                                const xfer_region *regions, int n_regions, void *dev, size_t dev_bytes,
+                                xfer_descs_plan *out);
+
+/*
+ * xfer_copy_descs - execute the plan: slab[dst_off + k] = *(src + k) for every
+ * descriptor, k < bytes.  slab (device) is slab_bytes long at least, 16-byte
+ * aligned, and must not overlap [src_lo, src_hi).
+ */
+XFER_API int xfer_copy_descs(const xfer_descs_plan *plan, void *slab, size_t slab_bytes, hipStream_t stream);
+
 /* -------------------------------------------- streamed two-rank all-reduce */
 
 /*

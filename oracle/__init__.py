@@ -63,6 +63,11 @@ def lib():
         L.oracle_gather.restype = I
         L.oracle_scatter.argtypes = [P, P, P, P, U64, U32, U32, U64, ctypes.POINTER(Region), I, P]
         L.oracle_scatter.restype = I
+        L.oracle_groups_plan.argtypes = [P, P, P, P, U64, U32, U32, U64, P, P, I, U64, P, U64,
+                                         ctypes.POINTER(U64), ctypes.POINTER(U64), P]
+        L.oracle_groups_plan.restype = I
+        L.oracle_copy_descs.argtypes = [P, U64, ctypes.POINTER(Region), I, P, U64]
+        L.oracle_copy_descs.restype = I
         _lib = L
     return _lib
 
@@ -206,3 +211,35 @@ def gather(t: RunTable, seg_bytes: int, regions, staging: np.ndarray | None = No
 def scatter(t: RunTable, seg_bytes: int, regions, staging: np.ndarray) -> None:
     reg = _regions(regions)
     _check(lib().oracle_scatter(*t._args(), seg_bytes, reg, len(regions), _p(staging)), "scatter")
+
+
+# ---------------------------------------------------------- coalesced fetch
+
+DESC = np.dtype([("src", "<u8"), ("dst_off", "<u8"), ("bytes", "<u8")])
+
+
+def groups_plan(t: RunTable, seg_bytes: int, regions, max_read_bytes: int = 32 << 20):
+    """regions: list of (device base, bytes).  Returns (descs, slab_bytes,
+    local offsets [n_lanes, n_blocks])."""
+    rb = np.array([b for b, _ in regions], np.uint64)
+    rs = np.array([n for _, n in regions], np.uint64)
+    n = ctypes.c_uint64(0)
+    slab = ctypes.c_uint64(0)
+    local = np.zeros((t.n_lanes, t.n_blocks), np.uint64)
+    rc = lib().oracle_groups_plan(*t._args(), seg_bytes, _p(rb), _p(rs), len(regions), max_read_bytes, None, 0,
+                                  ctypes.byref(n), ctypes.byref(slab), _p(local))
+    if rc not in (OK, EARG) or (rc == EARG and n.value == 0 and t.n_runs):
+        _check(rc, "groups_plan")
+    descs = np.zeros(max(1, n.value), DESC)
+    _check(lib().oracle_groups_plan(*t._args(), seg_bytes, _p(rb), _p(rs), len(regions), max_read_bytes,
+                                    _p(descs), n.value, ctypes.byref(n), ctypes.byref(slab), _p(local)),
+           "groups_plan")
+    return descs[:n.value].copy(), slab.value, local
+
+
+def copy_descs(descs: np.ndarray, regions, slab: np.ndarray) -> None:
+    """regions: list of (device base, host uint8 image)."""
+    d = np.ascontiguousarray(descs, dtype=DESC)
+    reg = _regions(regions)
+    _check(lib().oracle_copy_descs(_p(d) if d.size else None, d.size, reg, len(regions), _p(slab), slab.nbytes),
+           "copy_descs")

@@ -430,3 +430,170 @@ int oracle_scatter(const uint32_t *runs_per_lane, const uint64_t *run_base, cons
   free(addrs);
   return ORACLE_OK;
 }
+
+/* ------------------------------------------------- coalesced fetch planning */
+
+typedef struct {
+  uint64_t base;   /* remote address of block `start` */
+  int64_t stride;  /* 0 for a one-block run */
+  uint32_t lane, start, count, region;
+  uint64_t index;
+} run_info;
+
+static int by_region_then_base(const void *pa, const void *pb) {
+  const run_info *a = (const run_info *)pa, *b = (const run_info *)pb;
+  if (a->region != b->region) return a->region < b->region ? -1 : 1;
+  if (a->base != b->base) return a->base < b->base ? -1 : 1;
+  return a->index < b->index ? -1 : (a->index > b->index);
+}
+
+static uint64_t abs64(int64_t s) { return s < 0 ? (uint64_t)0 - (uint64_t)s : (uint64_t)s; }
+
+/*
+ * [RUNS] "What this PR does", the requester's plan, step by step:
+ *   2. decode the runs, bucket them per NUMA node (declared region), sort
+ *      each bucket by remote base;
+ *   3. group runs whose per-block chunks tile densely: same block range, same
+ *      stride, base-adjacent, and the grown chunk still fits the stride;
+ *   4. one slab carve and one coalesced read per dense group (chunks back to
+ *      back); other groups are read block by block into a dense mirror;
+ *      reads are split at max_read_bytes ("READ splitting");
+ *   5. rebuild: local(b) = group_local + (remote(b) - group_remote).
+ */
+int oracle_groups_plan(const uint32_t *runs_per_lane, const uint64_t *run_base, const int64_t *run_stride,
+                       const uint32_t *run_count, uint64_t n_runs, uint32_t n_lanes, uint32_t n_blocks,
+                       uint64_t seg_bytes, const uint64_t *region_base, const uint64_t *region_bytes, int n_regions,
+                       uint64_t max_read_bytes, oracle_desc *descs, uint64_t cap, uint64_t *n_descs,
+                       uint64_t *slab_bytes, uint64_t *local) {
+  if (max_read_bytes == 0 || seg_bytes == 0) return ORACLE_EARG;
+  run_info *runs = (run_info *)malloc((n_runs ? n_runs : 1) * sizeof(run_info));
+  if (!runs) return ORACLE_EARG;
+  /* step 2: decode */
+  uint64_t r = 0;
+  for (uint32_t l = 0; l < n_lanes; ++l) {
+    uint32_t start = 0;
+    for (uint32_t k = 0; k < runs_per_lane[l]; ++k, ++r) {
+      if (r >= n_runs || run_count[r] == 0) {
+        free(runs);
+        return ORACLE_ETABLE;
+      }
+      run_info *x = &runs[r];
+      x->base = run_base[r];
+      x->count = run_count[r];
+      x->stride = x->count > 1 ? run_stride[r] : 0;
+      x->lane = l;
+      x->start = start;
+      x->index = r;
+      uint64_t last;
+      if (!run_addr(x->base, x->stride, x->count - 1, &last)) {
+        free(runs);
+        return ORACLE_ETABLE;
+      }
+      const uint64_t lo = x->base < last ? x->base : last;
+      const uint64_t hi = (x->base > last ? x->base : last) + seg_bytes;
+      int found = -1;
+      for (int g = 0; g < n_regions && found < 0; ++g)
+        if (lo >= region_base[g] && hi <= region_base[g] + region_bytes[g]) found = g;
+      if (found < 0) {
+        free(runs);
+        return ORACLE_ERANGE;
+      }
+      x->region = (uint32_t)found;
+      start += x->count;
+    }
+    if (start != n_blocks) {
+      free(runs);
+      return ORACLE_ETABLE;
+    }
+  }
+  if (r != n_runs) {
+    free(runs);
+    return ORACLE_ETABLE;
+  }
+  /* bucket per region, sort by remote base */
+  qsort(runs, n_runs, sizeof(run_info), by_region_then_base);
+
+  uint64_t nd = 0, slab = 0;
+  uint64_t i = 0;
+  while (i < n_runs) {
+    /* step 3: grow a group from runs[i] */
+    const run_info *f = &runs[i];
+    uint64_t j = i + 1, chunk = seg_bytes;
+    while (j < n_runs) {
+      const run_info *x = &runs[j];
+      const int same_blocks = x->start == f->start && x->count == f->count;
+      const int adjacent = x->region == f->region && x->base == f->base + chunk;
+      const int fits = f->count == 1 || chunk + seg_bytes <= abs64(f->stride);
+      if (!(same_blocks && x->stride == f->stride && adjacent && fits)) break;
+      chunk += seg_bytes;
+      ++j;
+    }
+    /* step 4: carve and read */
+    const int dense = f->count == 1 || abs64(f->stride) == chunk;
+    const uint64_t group_local = slab;
+    uint64_t group_remote;
+    if (dense) {
+      const uint64_t span = f->count == 1 ? chunk : (uint64_t)f->count * abs64(f->stride);
+      group_remote = f->stride >= 0 ? f->base : f->base - (uint64_t)(f->count - 1) * abs64(f->stride);
+      for (uint64_t off = 0; off < span; off += max_read_bytes) {
+        const uint64_t n = span - off < max_read_bytes ? span - off : max_read_bytes;
+        if (nd < cap && descs) {
+          descs[nd].src = group_remote + off;
+          descs[nd].dst_off = group_local + off;
+          descs[nd].bytes = n;
+        }
+        ++nd;
+      }
+      slab += span;
+    } else {
+      group_remote = f->base;
+      for (uint32_t b = 0; b < f->count; ++b) {
+        uint64_t block_remote = 0;
+        run_addr(f->base, f->stride, b, &block_remote);
+        for (uint64_t off = 0; off < chunk; off += max_read_bytes) {
+          const uint64_t n = chunk - off < max_read_bytes ? chunk - off : max_read_bytes;
+          if (nd < cap && descs) {
+            descs[nd].src = block_remote + off;
+            descs[nd].dst_off = group_local + (uint64_t)b * chunk + off;
+            descs[nd].bytes = n;
+          }
+          ++nd;
+        }
+      }
+      slab += (uint64_t)f->count * chunk;
+    }
+    /* step 5: rebuild every segment's local address */
+    for (uint64_t k = i; k < j; ++k) {
+      const run_info *x = &runs[k];
+      for (uint32_t b = 0; b < x->count; ++b) {
+        uint64_t remote = 0;
+        run_addr(x->base, x->stride, b, &remote);
+        uint64_t loc;
+        if (dense) {
+          loc = group_local + (remote - group_remote);
+        } else {
+          uint64_t block_remote = 0;
+          run_addr(f->base, f->stride, b, &block_remote);
+          loc = group_local + (uint64_t)b * chunk + (remote - block_remote);
+        }
+        local[(uint64_t)x->lane * n_blocks + x->start + b] = loc;
+      }
+    }
+    i = j;
+  }
+  free(runs);
+  *n_descs = nd;
+  *slab_bytes = slab;
+  return nd <= cap ? ORACLE_OK : ORACLE_EARG;
+}
+
+int oracle_copy_descs(const oracle_desc *descs, uint64_t n_descs, const oracle_region *regions, int n_regions,
+                      uint8_t *slab, uint64_t slab_bytes) {
+  for (uint64_t d = 0; d < n_descs; ++d) {
+    const uint8_t *from = host_at(regions, n_regions, descs[d].src, descs[d].bytes);
+    if (!from || descs[d].dst_off > slab_bytes || slab_bytes - descs[d].dst_off < descs[d].bytes)
+      return ORACLE_ERANGE;
+    memcpy(slab + descs[d].dst_off, from, descs[d].bytes);
+  }
+  return ORACLE_OK;
+}

@@ -99,6 +99,25 @@ int oracle_scatter(const uint32_t *runs_per_lane, const uint64_t *run_base, cons
                    const uint32_t *run_count, uint64_t n_runs, uint32_t n_lanes, uint32_t n_blocks,
                    uint64_t seg_bytes, const oracle_region *regions, int n_regions, const uint8_t *staging);
 
+/* One contiguous read: bytes from device address src to slab offset dst_off. */
+typedef struct {
+  uint64_t src, dst_off, bytes;
+} oracle_desc;
+
+/* [RUNS] "What this PR does" steps 2-5 and "READ splitting": the descriptors
+ * of the coalesced fetch, the slab size, and every segment's slab offset
+ * (local[l * n_blocks + b]).  n_descs receives the count even when it
+ * exceeds cap (then ORACLE_EARG). */
+int oracle_groups_plan(const uint32_t *runs_per_lane, const uint64_t *run_base, const int64_t *run_stride,
+                       const uint32_t *run_count, uint64_t n_runs, uint32_t n_lanes, uint32_t n_blocks,
+                       uint64_t seg_bytes, const uint64_t *region_base, const uint64_t *region_bytes, int n_regions,
+                       uint64_t max_read_bytes, oracle_desc *descs, uint64_t cap, uint64_t *n_descs,
+                       uint64_t *slab_bytes, uint64_t *local);
+
+/* slab[d.dst_off + k] = bytes at d.src + k for every descriptor. */
+int oracle_copy_descs(const oracle_desc *descs, uint64_t n_descs, const oracle_region *regions, int n_regions,
+                      uint8_t *slab, uint64_t slab_bytes);
+
 #ifdef __cplusplus
 }
 #endif
