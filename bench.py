@@ -83,7 +83,8 @@ class Workload:
     seeded random order, so every lane breaks into many runs (the greedy
     table, and a second table with one run per segment, are both gathered)."""
 
-    def __init__(self, dev, tokens=TOKENS, shuffled=False, n_blocks=N_BLOCKS, seg=SEG, coalesced=False):
+    def __init__(self, dev, tokens=TOKENS, shuffled=False, n_blocks=N_BLOCKS, seg=SEG, coalesced=False,
+                 streamed=False):
         import numpy as np
         import torch
 
@@ -155,13 +156,36 @@ class Workload:
         self.dst_plan_buf = torch.zeros(x.runs_plan_bytes(self.dst_table), dtype=torch.uint8, device=dev)
         self.dst_plan = x.runs_prepare(self.dst_table, [(self.dst.data_ptr(), self.dst.numel())], True,
                                        self.dst_plan_buf)
+        self.streamed = streamed
+        if streamed:
+            # both ranks' rings and results, and four default-priority streams
+            self.send = [torch.zeros(2 * CHUNK // 2, dtype=torch.int16, device=dev) for _ in range(2)]
+            self.recv = [torch.zeros(2 * CHUNK // 2, dtype=torch.int16, device=dev) for _ in range(2)]
+            self.outs = [torch.zeros(n, dtype=torch.float32, device=dev) for _ in range(2)]
+            self.compute = [torch.cuda.Stream(device=dev) for _ in range(2)]
+            self.wire = [torch.cuda.Stream(device=dev) for _ in range(2)]
+            self.events = x.Events(6 * 2)
         torch.cuda.synchronize()
+
+    def _allreduce(self):
+        """One streamed all-reduce, ordered after and before the current stream."""
+        cur = self.torch.cuda.current_stream()
+        for s in self.compute + self.wire:
+            s.wait_stream(cur)
+        st = self.x.allreduce2_streamed((self.a, self.b), self.send, self.recv, self.outs, CHUNK, self.x.OUT_F32,
+                                        self.compute, self.wire, self.events)
+        if st != self.x.OK:
+            raise RuntimeError(f"xfer_allreduce2_streamed: {self.x.status_str(st)}")
+        for s in self.compute:
+            cur.wait_stream(s)
 
     def kernels(self):
         """(name, callable) in step order; each callable enqueues one call."""
         x = self.x
         n, nc = self.n, self.n_chunks
         ra, rb = self.ring_a, self.ring_b
+        if self.streamed:
+            return [("allreduce2_streamed", self._allreduce)]
         ks = [
             ("pack_rank0", lambda: x.pack_bf16(self.a, ra, CHUNK, 0, nc)),
             ("pack_rank1", lambda: x.pack_bf16(self.b, rb, CHUNK, 0, nc)),
@@ -179,6 +203,9 @@ class Workload:
         return ks
 
     def algorithmic_bytes(self):
+        if self.streamed:
+            # per rank: pack 6 B, wire copy 2 B read + 2 B written, combine F32 8 B per element
+            return {"allreduce2_streamed": 2 * 18 * self.n}
         extra = (("gather_per_segment",) if self.seg_plan is not None else ()) + \
             (("fetch_coalesced",) if self.fetch_plan is not None else ())
         ab = algorithmic_bytes(self.tokens, extra)
@@ -296,6 +323,14 @@ WORKLOADS = {
         "roofline_kernel": ("fetch_coalesced", "copy_descs (72 dense-group reads)", "descs_copy.hip",
                             "fetch_dense"),
     },
+    "streamed": {
+        "args": {"tokens": TOKENS, "shuffled": False, "streamed": True},
+        "describe": "streamed two-rank all-reduce of two 2048x5120 F32 partials through 512 KiB BF16 chunks and two "
+                    "slots per rank: pack, device-to-device wire copy, F32 combine for both ranks, ordered by events "
+                    "on four streams (both ranks on one GPU)",
+        "roofline_kernel": ("allreduce2_streamed", "allreduce2_streamed (40 chunks x 2 ranks x pack/copy/combine)",
+                            None, None),
+    },
 }
 
 
@@ -348,7 +383,7 @@ def main():
     g_gbs = ab[rk] / (kms[rk] * 1e-3) / 1e9
     roofline = {"kernel": rk_label, "bound": "hbm", "achieved": round(g_gbs, 1),
                 "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(g_gbs / PEAK_HBM_GBS, 4),
-                "traffic": measured_traffic(rk_file, rk_key)}
+                "traffic": measured_traffic(rk_file, rk_key) if rk_file else None}
     line = {
         "metric": "achieved HBM GB/s (and % of peak) for pack+combine and run-table segment gather",
         "value": round(value, 1),
@@ -368,8 +403,9 @@ def main():
             "parallelism": "single GPU; both ranks emulated in one HBM",
         },
         "kernels": kernels,
-        "pack_combine_GBps": round((ab["pack_rank0"] + ab["pack_rank1"] + ab["combine_f32"]) /
-                                   ((kms["pack_rank0"] + kms["pack_rank1"] + kms["combine_f32"]) * 1e-3) / 1e9, 1),
+        "pack_combine_GBps": (round((ab["pack_rank0"] + ab["pack_rank1"] + ab["combine_f32"]) /
+                                    ((kms["pack_rank0"] + kms["pack_rank1"] + kms["combine_f32"]) * 1e-3) / 1e9, 1)
+                              if "pack_rank0" in ab else None),
         "roofline": roofline,
         "cpu_baseline": None,
     }

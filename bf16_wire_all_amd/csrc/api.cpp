@@ -225,6 +225,7 @@ int xfer_pack_bf16(const float *src, size_t n, uint16_t *ring, size_t ring_bytes
   const uint64_t n_chunks = n / ce + (n % ce != 0);
   if (chunk_end > n_chunks) return XFER_E_INVAL;
   if (n > SIZE_MAX / 4) return XFER_E_INVAL;
+  if (std::min<uint64_t>(chunk_end * ce, n) - chunk_begin * ce > xfer::kMaxStreamElems) return XFER_E_UNSUPPORTED;
   if (overlaps((uintptr_t)src, (uint64_t)n * 4, (uintptr_t)ring, ring_bytes)) return XFER_E_INVAL;
   const uint64_t e0 = chunk_begin * ce;
   const uint64_t e1 = std::min<uint64_t>(chunk_end * ce, n);
@@ -238,6 +239,7 @@ int xfer_combine2(const uint16_t *a, const uint16_t *b, size_t n, void *out, int
   if (n == 0) return XFER_OK;
   if (!a || !b || !out || !aligned16(a) || !aligned16(b) || !aligned16(out)) return XFER_E_INVAL;
   if (n > SIZE_MAX / 4) return XFER_E_INVAL;
+  if (n > xfer::kMaxStreamElems) return XFER_E_UNSUPPORTED;
   const uint64_t out_bytes = (uint64_t)n * (out_mode == XFER_OUT_F32 ? 4 : 2);
   const uintptr_t o = (uintptr_t)out;
   const bool in_place = out_mode == XFER_OUT_BF16 && (out == (const void *)a || out == (const void *)b);
@@ -284,6 +286,7 @@ int xfer_argmax_merge(const xfer_shard *s0, const xfer_shard *s1, int mode, void
     span[i] = (last_row + s[i]->ncols) * 2;
   }
   const uint32_t splits = xfer::argmax_splits(rows, s0->ncols, s1->ncols);
+  if ((uint64_t)rows * 2 * splits > xfer::kMaxGridBlocks) return XFER_E_UNSUPPORTED;
   const uint64_t need = xfer::argmax_workspace_bytes(rows, splits);
   if (!out || !aligned16(out)) return XFER_E_INVAL;
   if (!workspace || !aligned16(workspace) || workspace_bytes < need) return XFER_E_INVAL;
@@ -367,6 +370,7 @@ int xfer_runs_prepare(const xfer_run_table *t, const xfer_region *regions, int n
   if (st != XFER_OK) return st;
   if (!out) return XFER_E_INVAL;
   const Layout L = layout_for(t);
+  if ((uint64_t)t->n_lanes * L.n_tiles * L.pieces > xfer::kMaxGridBlocks) return XFER_E_UNSUPPORTED;
   if (L.total && (!dev || !aligned16(dev) || dev_bytes < L.total)) return XFER_E_INVAL;
 
   // Host image of the plan: per (lane, group of blocks) the run covering the
@@ -426,7 +430,7 @@ int xfer_gather_runs(const xfer_runs_plan *plan, void *staging, size_t staging_b
   if (!plan_ok(plan)) return XFER_E_INVAL;
   const int st = staging_check(plan, (uintptr_t)staging, staging_bytes);
   if (st != XFER_OK) return st;
-  if ((uint64_t)plan->n_lanes * plan->n_tiles * plan->pieces > (uint64_t)INT32_MAX) return XFER_E_UNSUPPORTED;
+  if ((uint64_t)plan->n_lanes * plan->n_tiles * plan->pieces > xfer::kMaxGridBlocks) return XFER_E_UNSUPPORTED;
   if (xfer::launch_gather(view_of(plan), staging, stream) != hipSuccess) return XFER_E_DEVICE;
   return XFER_OK;
 }
@@ -437,7 +441,7 @@ int xfer_scatter_runs(const void *staging, size_t staging_bytes, const xfer_runs
   if (!plan_ok(plan)) return XFER_E_INVAL;
   const int st = staging_check(plan, (uintptr_t)staging, staging_bytes);
   if (st != XFER_OK) return st;
-  if ((uint64_t)plan->n_lanes * plan->n_tiles * plan->pieces > (uint64_t)INT32_MAX) return XFER_E_UNSUPPORTED;
+  if ((uint64_t)plan->n_lanes * plan->n_tiles * plan->pieces > xfer::kMaxGridBlocks) return XFER_E_UNSUPPORTED;
   if (xfer::launch_scatter(view_of(plan), staging, stream) != hipSuccess) return XFER_E_DEVICE;
   return XFER_OK;
 }

@@ -1,44 +1,45 @@
 // Execution of a descriptor list: every descriptor is one contiguous copy of
-// `bytes` from a device address into the slab.  Work unit: one 256-thread
-// workgroup per 8 KiB piece of a descriptor (2 nontemporal 16-byte vectors
-// per thread), pieces of one descriptor on consecutive workgroups so the chip
-// streams contiguous ranges.  The grid is n_descs x max_pieces; workgroups
-// past a short descriptor's end exit at once.  The same short-lived
-// workgroup shape measured fastest for the segment gather.
+// `bytes` from a device address into the slab.  A descriptor is cut into
+// 4 KiB units and its two halves are walked side by side: workgroup piece c
+// copies unit c and unit c + ceil(units / 2), each thread one 16-byte vector
+// of each, every load followed by its store (nontemporal both ways).  On
+// MI355X this two-stream shape measured 6.4-6.7 TB/s for a plain 2.36 GB copy
+// against 5.9 TB/s for one contiguous 8 KiB piece per workgroup with both
+// loads issued first.  The grid is n_descs x max_pieces (max_pieces = the
+// largest descriptor's ceil(bytes / 8 KiB)); workgroups past a shorter
+// descriptor's half exit at once.
 #include "internal.h"
 
 namespace xfer {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr uint32_t kVecsPerPiece = kDescPieceBytes / 16;  // 512
+constexpr uint32_t kUnitBytes = kDescPieceBytes / 2;  // 4 KiB: one 16-byte vector per thread
 
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(1))) v4u g_v4u;
 
-__global__ __launch_bounds__(kThreads) void copy_descs_kernel(const xfer_desc *descs, uint32_t max_pieces,
-                                                              uint8_t *slab) {
-  const uint64_t d = blockIdx.x / max_pieces;
-  const uint32_t piece = blockIdx.x % max_pieces;
-  const xfer_desc desc = descs[d];
-  const uint64_t off = (uint64_t)piece * kDescPieceBytes;
-  if (off >= desc.bytes) return;
-  const uint64_t left = desc.bytes - off;
-  const uint32_t nvec = (uint32_t)((left < kDescPieceBytes ? left : kDescPieceBytes) / 16);
+__device__ __forceinline__ void copy_unit(const xfer_desc &desc, uint8_t *slab, uint64_t unit) {
+  const uint64_t off = unit * kUnitBytes + 16u * threadIdx.x;
+  if (off >= desc.bytes) return;  // bytes is a multiple of 16: the whole vector is inside
   const g_v4u *src = reinterpret_cast<const g_v4u *>(desc.src + off);
   g_v4u *dst = reinterpret_cast<g_v4u *>((uint64_t)(slab + desc.dst_off + off));
-  const uint32_t v = threadIdx.x;
-  if (v + kThreads < nvec) {
-    const v4u a = __builtin_nontemporal_load(&src[v]);
-    const v4u b = __builtin_nontemporal_load(&src[v + kThreads]);
-    __builtin_nontemporal_store(a, &dst[v]);
-    __builtin_nontemporal_store(b, &dst[v + kThreads]);
-  } else {
-    for (uint32_t i = v; i < nvec; i += kThreads) __builtin_nontemporal_store(__builtin_nontemporal_load(&src[i]), &dst[i]);
-  }
+  __builtin_nontemporal_store(__builtin_nontemporal_load(src), dst);
 }
 
-static_assert(kVecsPerPiece == 2 * kThreads, "two vectors per thread per piece");
+__global__ __launch_bounds__(kThreads) void copy_descs_kernel(const xfer_desc *descs, uint32_t max_pieces,
+                                                              uint8_t *slab) {
+  const uint32_t d = blockIdx.x / max_pieces;
+  const uint32_t piece = blockIdx.x - d * max_pieces;
+  const xfer_desc desc = descs[d];
+  const uint64_t n_units = (desc.bytes + kUnitBytes - 1) / kUnitBytes;
+  const uint64_t half = (n_units + 1) / 2;  // == ceil(bytes / 8 KiB)
+  if (piece >= half) return;
+  copy_unit(desc, slab, piece);
+  if (piece + half < n_units) copy_unit(desc, slab, piece + half);
+}
+
+static_assert(kUnitBytes == 16 * kThreads, "one vector per thread per unit");
 
 }  // namespace
 

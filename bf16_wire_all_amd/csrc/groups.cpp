@@ -170,7 +170,7 @@ int xfer_descs_prepare(const xfer_desc *descs, uint64_t n_descs, uint64_t slab_b
   for (size_t i = 1; i < dst.size(); ++i)
     if (dst[i].first < dst[i - 1].first + dst[i - 1].second) return XFER_E_OVERLAP;
   const uint64_t pieces = (max_bytes + xfer::kDescPieceBytes - 1) / xfer::kDescPieceBytes;
-  if (pieces > UINT32_MAX || (n_descs && pieces * n_descs > (uint64_t)INT32_MAX)) return XFER_E_UNSUPPORTED;
+  if (pieces > UINT32_MAX || (n_descs && pieces * n_descs > xfer::kMaxGridBlocks)) return XFER_E_UNSUPPORTED;
   const uint64_t need = xfer_descs_plan_bytes(n_descs);
   if (need && (!dev || ((uintptr_t)dev & 15u) || dev_bytes < need)) return XFER_E_INVAL;
   if (n_descs && hipMemcpy(dev, descs, n_descs * sizeof(xfer_desc), hipMemcpyHostToDevice) != hipSuccess)

@@ -22,6 +22,12 @@ static inline hipError_t launch(void (*kernel)(KArgs...), dim3 grid, dim3 block,
   return hipLaunchKernel((const void *)kernel, grid, block, argv, lds, stream);
 }
 
+// A dispatch holds at most 2^32 - 1 work-items along x (the packet's grid
+// size is a 32-bit work-item count): 2^24 - 1 workgroups of 256 threads.
+constexpr uint64_t kMaxGridBlocks = (1ull << 24) - 1;
+// Pack and combine move 2048 elements per workgroup.
+constexpr uint64_t kMaxStreamElems = kMaxGridBlocks * 2048;
+
 // ---- host helpers shared by the entry points (api.cpp)
 int validate_table(const xfer_run_table *t, const xfer_region *regions, int n_regions, int is_dst,
                    uint64_t *span_lo, uint64_t *span_hi);

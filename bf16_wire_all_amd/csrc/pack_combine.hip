@@ -7,11 +7,13 @@
 //   - a thread handles "quads" of 4 consecutive elements, so every load and
 //     store instruction of a wave covers one contiguous span (1 KiB of F32,
 //     512 B of BF16): fully coalesced 128-bit / 64-bit accesses;
-//   - each workgroup streams one contiguous chunk of 1024 quads in a single
-//     pass, every thread issuing its 4 loads before its first store, and the
-//     grid has one workgroup per chunk.  On MI355X many short workgroups over
-//     contiguous chunks kept HBM busier than a grid-stride loop (16384 x 5120
-//     pack: 6.2 TB/s against 5.4-5.9 TB/s);
+//   - many short workgroups, each streaming one contiguous chunk of 512 quads
+//     in a single pass (2 quads per thread, each load followed by its store).
+//     Measured on MI355X after a 2.36 GB copy, against 1024-quad chunks with
+//     the loads issued first: pack 16384 x 5120 6.4 TB/s (was 6.1), combine
+//     6.4 (6.0); at 2048 x 5120 pack 4.5 (4.2), combine 5.0 (4.5).  Pairing
+//     units from the two halves of the operands, which helps plain copies,
+//     measured no better here;
 //   - loads and stores carry the nontemporal hint: each byte is touched once
 //     (cold 2048 x 5120 pack: 4.5 TB/s with it, 2.5 TB/s without).
 #include "internal.h"
@@ -20,7 +22,7 @@ namespace xfer {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kQuadsPerThread = 4;
+constexpr int kQuadsPerThread = 2;
 constexpr uint64_t kQuadsPerBlock = (uint64_t)kThreads * kQuadsPerThread;
 
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
@@ -97,19 +99,10 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(const uint4 *__restrict_
     reinterpret_cast<uint16_t *>(ring)[d] = (uint16_t)bf16_rne(__float_as_uint(s1[threadIdx.x]));
   }
   const uint64_t q0 = (uint64_t)blockIdx.x * kQuadsPerBlock + threadIdx.x;
-  if (q0 + (kQuadsPerThread - 1) * kThreads < n_quads) {
-    uint4 v[kQuadsPerThread];
 #pragma unroll
-    for (int u = 0; u < kQuadsPerThread; ++u) v[u] = ld(&src[q0 + u * kThreads]);
-#pragma unroll
-    for (int u = 0; u < kQuadsPerThread; ++u) {
-      uint64_t d = q0 + u * kThreads + slot0_q;
-      if (d >= ring_quads) d -= ring_quads;
-      st(&ring[d], pack_quad(v[u]));
-    }
-  } else {  // the last, partial chunk
-    const uint64_t q_end = min(n_quads, ((uint64_t)blockIdx.x + 1) * kQuadsPerBlock);
-    for (uint64_t q = q0; q < q_end; q += kThreads) {
+  for (int u = 0; u < kQuadsPerThread; ++u) {
+    const uint64_t q = q0 + u * kThreads;
+    if (q < n_quads) {
       uint64_t d = q + slot0_q;
       if (d >= ring_quads) d -= ring_quads;
       st(&ring[d], pack_quad(ld(&src[q])));
@@ -119,6 +112,15 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(const uint4 *__restrict_
 
 // In BF16 mode out may be a or b itself: every thread reads its own quads
 // before writing them and no other thread touches them.
+template <int MODE>
+__device__ __forceinline__ void combine_quad(const uint2 *a, const uint2 *b, void *out, uint64_t q) {
+  const uint4 s = sum_quad(ld(&a[q]), ld(&b[q]));
+  if (MODE == XFER_OUT_F32)
+    st(&reinterpret_cast<uint4 *>(out)[q], s);
+  else
+    st(&reinterpret_cast<uint2 *>(out)[q], pack_quad(s));
+}
+
 template <int MODE>
 __global__ __launch_bounds__(kThreads) void combine_kernel(const uint2 *a, const uint2 *b, void *out,
                                                            uint64_t n_quads, uint32_t tail) {
@@ -131,30 +133,10 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const uint2 *a, const
       reinterpret_cast<uint16_t *>(out)[e] = (uint16_t)bf16_rne(s);
   }
   const uint64_t q0 = (uint64_t)blockIdx.x * kQuadsPerBlock + threadIdx.x;
-  if (q0 + (kQuadsPerThread - 1) * kThreads < n_quads) {
-    uint2 va[kQuadsPerThread], vb[kQuadsPerThread];
 #pragma unroll
-    for (int u = 0; u < kQuadsPerThread; ++u) {
-      va[u] = ld(&a[q0 + u * kThreads]);
-      vb[u] = ld(&b[q0 + u * kThreads]);
-    }
-#pragma unroll
-    for (int u = 0; u < kQuadsPerThread; ++u) {
-      const uint4 s = sum_quad(va[u], vb[u]);
-      if (MODE == XFER_OUT_F32)
-        st(&reinterpret_cast<uint4 *>(out)[q0 + u * kThreads], s);
-      else
-        st(&reinterpret_cast<uint2 *>(out)[q0 + u * kThreads], pack_quad(s));
-    }
-  } else {  // the last, partial chunk
-    const uint64_t q_end = min(n_quads, ((uint64_t)blockIdx.x + 1) * kQuadsPerBlock);
-    for (uint64_t q = q0; q < q_end; q += kThreads) {
-      const uint4 s = sum_quad(ld(&a[q]), ld(&b[q]));
-      if (MODE == XFER_OUT_F32)
-        st(&reinterpret_cast<uint4 *>(out)[q], s);
-      else
-        st(&reinterpret_cast<uint2 *>(out)[q], pack_quad(s));
-    }
+  for (int u = 0; u < kQuadsPerThread; ++u) {
+    const uint64_t q = q0 + u * kThreads;
+    if (q < n_quads) combine_quad<MODE>(a, b, out, q);
   }
 }
 

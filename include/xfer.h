@@ -88,7 +88,8 @@ XFER_API const char *xfer_status_str(int status);
  * chunk_bytes is 0 or not a multiple of 16, if ring_bytes is not a non-zero
  * multiple of chunk_bytes, if chunk_end - chunk_begin > R (two chunks of one
  * call would share a slot), if a named chunk starts at or past n, or if src
- * and ring overlap.
+ * and ring overlap; XFER_E_UNSUPPORTED if the call's range holds more than
+ * (2^24 - 1) * 2048 elements (one launch).
  */
 XFER_API int xfer_pack_bf16(const float *src, size_t n, uint16_t *ring, size_t ring_bytes, size_t chunk_bytes,
                    size_t chunk_begin, size_t chunk_end, hipStream_t stream);
@@ -112,7 +113,8 @@ enum { XFER_OUT_F32 = 0, XFER_OUT_BF16 = 1 };
  *
  * Errors: XFER_E_INVAL for NULL or misaligned pointers, an unknown out_mode,
  * or an output that overlaps an input (except out == a_rank0 or
- * out == b_rank1 exactly in BF16 mode, which is computed in place).
+ * out == b_rank1 exactly in BF16 mode, which is computed in place);
+ * XFER_E_UNSUPPORTED for n above (2^24 - 1) * 2048 (one launch).
  */
 XFER_API int xfer_combine2(const uint16_t *a_rank0, const uint16_t *b_rank1, size_t n, void *out, int out_mode,
                   hipStream_t stream);
@@ -167,7 +169,8 @@ typedef struct {
  * be multiples of 16), different row counts, ncols == 0, shards whose id
  * ranges overlap, col_offset + ncols > 2^31, an unknown mode, a small
  * workspace, or an output overlapping the logits or the workspace;
- * XFER_E_UNSUPPORTED for a shard wider than 65536 columns.
+ * XFER_E_UNSUPPORTED for a shard wider than 65536 columns or more than
+ * 2^23 - 1 rows.
  */
 XFER_API size_t xfer_argmax_workspace_bytes(uint32_t rows, uint32_t ncols0, uint32_t ncols1);
 XFER_API int xfer_argmax_merge(const xfer_shard *s0, const xfer_shard *s1, int mode, void *out, void *workspace,
@@ -274,7 +277,9 @@ XFER_API size_t xfer_runs_plan_bytes(const xfer_run_table *t);
  * write the kernels' form of it into dev (device, 16-byte aligned, at least
  * xfer_runs_plan_bytes(t) bytes) with a blocking host-to-device copy, and
  * fill *out.  Returns the validation status, XFER_E_INVAL for a small or
- * misaligned dev, or XFER_E_DEVICE if the copy fails.
+ * misaligned dev, XFER_E_UNSUPPORTED if the set needs more than 2^24 - 1
+ * workgroups (about 8 KiB each: a set of more than ~128 GiB), or
+ * XFER_E_DEVICE if the copy fails.
  */
 XFER_API int xfer_runs_prepare(const xfer_run_table *t, const xfer_region *regions, int n_regions, int is_dst, void *dev,
                       size_t dev_bytes, xfer_runs_plan *out);
@@ -370,6 +375,8 @@ XFER_API size_t xfer_descs_plan_bytes(uint64_t n_descs);
  * no source range wraps or leaves the declared regions (XFER_E_RANGE), the
  * destination ranges lie in [0, slab_bytes) and are pairwise disjoint
  * (XFER_E_OVERLAP).  dev: device, 16-byte aligned, xfer_descs_plan_bytes().
+ * XFER_E_UNSUPPORTED if n_descs times the largest descriptor's 8 KiB pieces
+ * exceeds 2^24 - 1 (the kernel's grid).
  */
 XFER_API int xfer_descs_prepare(const xfer_desc *descs, uint64_t n_descs, uint64_t slab_bytes,
                                 const xfer_region *regions, int n_regions, void *dev, size_t dev_bytes,

@@ -232,3 +232,29 @@ def test_plan_bytes_dense_config():
     nb = x.runs_plan_bytes(t)
     # 576 runs * 20 B plus a tile index of 576 lanes * 33 entries * 4 B
     assert nb < 128 * 1024
+
+
+def test_launch_size_limits():
+    """Requests whose one launch would need more than 2^24 - 1 workgroups of
+    256 threads (the dispatch's 32-bit work-item count) are refused on the
+    host, before any device call."""
+    big = 1 << 40
+    max_stream = ((1 << 24) - 1) * 2048
+    # pack: two 2^34-element chunks in one call
+    assert x.pack_bf16_raw(0x100000, 1 << 36, big, 1 << 36, 1 << 35, 0, 2, stream=S0) == x.E_UNSUPPORTED
+    assert x.combine2_raw(0x100000, big, max_stream + 4, 2 * big, 0, stream=S0) == x.E_UNSUPPORTED
+    rows = 1 << 23
+    s0 = x.shard(0x100000, 1024, rows, 512, 0)
+    s1 = x.shard(0x100000 + 1024, 1024, rows, 512, 512)
+    assert x.argmax_merge_raw(s0, s1, 0, big, 2 * big, 1 << 30, stream=S0) == x.E_UNSUPPORTED
+    # gather: one lane of 2^25 blocks of 4 KiB (2^24 tiles of 2 blocks)
+    t = _table([1], [big], [4096], [1 << 25], 1 << 25, seg=4096)
+    st, _ = x.runs_prepare_status(t, [(big, 1 << 37)], False, 0x1000, 1 << 30)
+    assert st == x.E_UNSUPPORTED
+    # descriptors: one read of 2^24 pieces of 8 KiB
+    d = np.array([(big, 0, 1 << 37)], x.DESC)
+    st, _ = x.descs_prepare_status(d, 1 << 37, [(big, 1 << 38)], 0x1000, 1 << 20)
+    assert st == x.E_UNSUPPORTED
+    d = np.array([(big, 0, (1 << 37) - 8192)], x.DESC)                  # one piece fewer: accepted
+    st, _ = x.descs_prepare_status(d, 1 << 37, [(big, 1 << 38)], 0, 0)
+    assert st == x.E_INVAL                                              # ...up to the missing device buffer
