@@ -53,6 +53,10 @@ def lib():
         L.oracle_sum2_f32.restype = U32
         L.oracle_combine2.argtypes = [P, P, S, P, I]
         L.oracle_combine2.restype = I
+        L.oracle_sum2_f32_f32.argtypes = [U32, U32]
+        L.oracle_sum2_f32_f32.restype = U32
+        L.oracle_combine2_f32.argtypes = [P, P, S, P, I]
+        L.oracle_combine2_f32.restype = I
         L.oracle_argmax_merge.argtypes = [ctypes.POINTER(Shard), ctypes.POINTER(Shard), I, P]
         L.oracle_argmax_merge.restype = I
         L.oracle_runs_encode.argtypes = [P, U32, U32, P, P, P, P, U64, ctypes.POINTER(U64)]
@@ -117,6 +121,20 @@ def combine2(a: np.ndarray, b: np.ndarray, mode: int) -> np.ndarray:
     assert a.size == b.size
     out = np.empty(a.size, dtype=np.uint32 if mode == 0 else np.uint16)
     _check(lib().oracle_combine2(_p(a), _p(b), a.size, _p(out), mode), "combine2")
+    return out
+
+
+def sum2_f32_f32_scalar(a_bits: int, b_bits: int) -> int:
+    return int(lib().oracle_sum2_f32_f32(a_bits, b_bits))
+
+
+def combine2_f32(a: np.ndarray, b: np.ndarray, mode: int) -> np.ndarray:
+    """F32-wire combine: a, b F32 values (or their uint32 bit patterns)."""
+    a = np.ascontiguousarray(a).view(np.float32).reshape(-1)
+    b = np.ascontiguousarray(b).view(np.float32).reshape(-1)
+    assert a.size == b.size
+    out = np.empty(a.size, dtype=np.uint32 if mode == 0 else np.uint16)
+    _check(lib().oracle_combine2_f32(_p(a), _p(b), a.size, _p(out), mode), "combine2_f32")
     return out
 
 

@@ -134,6 +134,41 @@ int oracle_combine2(const uint16_t *a, const uint16_t *b, size_t n, void *out, i
   return ORACLE_OK;
 }
 
+/*
+ * [TP2] "Layout" and "Collectives": the drafter's all-reduce pushes the F32
+ * partials themselves (no BF16 wire) and adds them in F32, rank 0's value
+ * first on both ranks; the sum is then rounded to BF16 (or kept in F32, the
+ * debug oracle's "optional BF16 rounding").  One IEEE binary32 addition,
+ * round to nearest even, subnormals kept; a NaN sum is written as the
+ * canonical 0x7FC00000, as for the BF16-wire sum.
+ */
+uint32_t oracle_sum2_f32_f32(uint32_t a_bits, uint32_t b_bits) {
+  float fa, fb;
+  memcpy(&fa, &a_bits, 4);
+  memcpy(&fb, &b_bits, 4);
+  float s = fa + fb;
+  uint32_t r;
+  memcpy(&r, &s, 4);
+  if ((r & 0x7FFFFFFFu) > 0x7F800000u) r = 0x7FC00000u;
+  return r;
+}
+
+/* mode 0: out[i] = the F32 sum; mode 1: that sum rounded to BF16 (RNE). */
+int oracle_combine2_f32(const float *a, const float *b, size_t n, void *out, int mode) {
+  if (mode != 0 && mode != 1) return ORACLE_EARG;
+  for (size_t i = 0; i < n; ++i) {
+    uint32_t ab, bb;
+    memcpy(&ab, &a[i], 4);
+    memcpy(&bb, &b[i], 4);
+    const uint32_t s = oracle_sum2_f32_f32(ab, bb);
+    if (mode == 0)
+      memcpy((uint8_t *)out + 4 * i, &s, 4);
+    else
+      ((uint16_t *)out)[i] = oracle_bf16_rne(s);
+  }
+  return ORACLE_OK;
+}
+
 /* ---------------------------------------------------------------- argmax */
 
 typedef struct {

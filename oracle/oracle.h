@@ -54,6 +54,11 @@ uint32_t oracle_sum2_f32(uint16_t a_rank0, uint16_t b_rank1);
 /* mode 0: out is float[n]; mode 1: out is BF16 bits uint16_t[n]. */
 int oracle_combine2(const uint16_t *a_rank0, const uint16_t *b_rank1, size_t n, void *out, int mode);
 
+/* F32-wire variant ([TP2]): sum of two F32 values in binary32 (F32 bits),
+ * and its array form; mode 0 F32 out, mode 1 BF16 out. */
+uint32_t oracle_sum2_f32_f32(uint32_t a_bits, uint32_t b_bits);
+int oracle_combine2_f32(const float *a_rank0, const float *b_rank1, size_t n, void *out, int mode);
+
 /* One shard's view of a row block of BF16 logits. */
 typedef struct {
   const uint16_t *ptr;   /* element (0, 0) of the shard           */

@@ -139,3 +139,41 @@ def bf16_bits_of_exact_sum(a: int, b: int) -> int:
     if r == 0 and s < 0:
         return 0x8000
     return r
+
+
+def exact_sum_f32(a: int, b: int):
+    """Exact sum of two F32 values given as bit patterns, with the IEEE rules
+    for infinities and NaN (the sign of an exact zero is the caller's)."""
+    x, y = f32_fraction(a), f32_fraction(b)
+    if x is NAN or y is NAN:
+        return NAN
+    if isinstance(x, float) or isinstance(y, float):
+        if isinstance(x, float) and isinstance(y, float) and x != y:
+            return NAN
+        return x if isinstance(x, float) else y
+    return x + y
+
+
+def f32_bits_of_exact_f32_sum(a: int, b: int) -> int:
+    """IEEE binary32 round-to-nearest-even of the exact sum of two F32
+    values, as bits; NaN canonical 0x7FC00000; an exact zero sum is +0 unless
+    both operands are -0.  Quantised with round-half-even on Fractions in
+    binary32's grid, as f32_bits_of_exact_sum_rounded does for BF16 inputs."""
+    s = exact_sum_f32(a, b)
+    if s is NAN:
+        return 0x7FC00000
+    if isinstance(s, float):
+        return 0x7F800000 if s > 0 else 0xFF800000
+    if s == 0:
+        return 0x80000000 if (a >> 31) and (b >> 31) else 0
+    neg = s < 0
+    mag = -s if neg else s
+    e = max(_floor_log2(mag), -126)
+    quantum = Fraction(2) ** (e - 23)
+    v = round(mag / quantum) * quantum
+    if v >= Fraction(2) ** 128:
+        return 0xFF800000 if neg else 0x7F800000
+    if v == 0:
+        return 0x80000000 if neg else 0
+    bits = struct.unpack("<I", struct.pack("<f", float(v)))[0]
+    return bits | (0x80000000 if neg else 0)

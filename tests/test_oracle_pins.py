@@ -207,6 +207,70 @@ def test_combine_f32_matches_numpy_and_identities():
     assert oracle.sum2_f32_scalar(0x7F80, 0xFF80) == 0x7FC00000
 
 
+# ---------------------------------------------------- F32-wire combine ([TP2])
+
+def _f32_wire_pairs():
+    """Structured F32 pairs: special values, ties of the binary32 grid,
+    overflow, subnormal sums and cancellation, and random pairs of close
+    exponents (where rounding happens)."""
+    special = [0x00000000, 0x80000000, 0x7F800000, 0xFF800000, 0x7FC00000, 0x7F800001, 0xFFC12345,
+               0x3F800000, 0xBF800000, 0x7F7FFFFF, 0xFF7FFFFF, 0x00000001, 0x80000001, 0x00800000,
+               0x807FFFFF, 0x007FFFFF, 0x33800000, 0xB3800000]
+    pairs = [(x, y) for x in special for y in special]
+    pairs += [
+        (0x3F800000, 0x33800000),   # 1 + 2^-24: a tie, stays at the even 1
+        (0x3F800001, 0x33800000),   # (1 + 2^-23) + 2^-24: a tie, goes up to the even 1 + 2^-22
+        (0x3F800000, 0x33800001),   # just above the tie: rounds up
+        (0x7F7FFFFF, 0x73000000),   # FLT_MAX + half its ulp: tie at the top, rounds to infinity
+        (0x7F7FFFFF, 0x72FFFFFF),   # just below: stays FLT_MAX
+        (0x00400000, 0x00400000),   # two subnormals sum to the smallest normal
+        (0x00800001, 0x80800000),   # normal - normal = smallest subnormal
+    ]
+    w = dg.random_u64(12000, 0xF32F32)
+    for v in w:
+        v = int(v)
+        a = v & 0xFFFFFFFF
+        e = (a >> 23) & 0xFF
+        de = (v >> 32) % 40
+        e2 = max(0, min(254, e - de if (v >> 40) & 1 else e + de))
+        b = ((v >> 41) & 1) << 31 | e2 << 23 | ((v >> 42) * 0x9E3779B1) & 0x7FFFFF
+        pairs.append((a, b))
+    return pairs
+
+
+def test_f32_wire_sum_exact_rationals():
+    pairs = _f32_wire_pairs()
+    a = np.array([p[0] for p in pairs], np.uint32)
+    b = np.array([p[1] for p in pairs], np.uint32)
+    got = oracle.combine2_f32(a, b, 0)
+    got16 = oracle.combine2_f32(a, b, 1)
+    for i, (x, y) in enumerate(pairs):
+        want = exact.f32_bits_of_exact_f32_sum(x, y)
+        assert int(got[i]) == want, (hex(x), hex(y), hex(int(got[i])), hex(want))
+        # the page's order: the F32 sum first, then its BF16 rounding
+        assert int(got16[i]) == exact.rne_bf16_of_f32_bits(want), (hex(x), hex(y))
+
+
+def test_f32_wire_rounds_twice_as_the_page_orders():
+    """fp32 sum, then BF16: 1 + 2^-8 + 2^-30 is 1 + 2^-8 in binary32, a BF16
+    tie that goes to the even 1.0; one rounding of the exact sum would give
+    the next BF16 value up."""
+    a, b = 0x3F808000, 0x30800000
+    assert oracle.sum2_f32_f32_scalar(a, b) == 0x3F808000
+    assert int(oracle.combine2_f32(np.array([a], np.uint32), np.array([b], np.uint32), 1)[0]) == 0x3F80
+
+
+def test_f32_wire_matches_numpy_and_commutes():
+    w = dg.random_u64(1 << 20, 0xF32A)
+    a = (w & 0xFFFFFFFF).astype(np.uint32)
+    b = (w >> 32).astype(np.uint32)
+    with np.errstate(all="ignore"):
+        ref = (a.view(np.float32) + b.view(np.float32)).view(np.uint32).copy()
+    ref[(ref & 0x7FFFFFFF) > 0x7F800000] = 0x7FC00000
+    assert np.array_equal(oracle.combine2_f32(a, b, 0), ref)
+    assert np.array_equal(oracle.combine2_f32(b, a, 0), ref)
+
+
 # ------------------------------------------------------------------ argmax
 
 def _brute_top2(vals_bits):
