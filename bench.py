@@ -84,7 +84,7 @@ class Workload:
     table, and a second table with one run per segment, are both gathered)."""
 
     def __init__(self, dev, tokens=TOKENS, shuffled=False, n_blocks=N_BLOCKS, seg=SEG, coalesced=False,
-                 streamed=False):
+                 streamed=False, f32wire=False):
         import numpy as np
         import torch
 
@@ -156,6 +156,12 @@ class Workload:
         self.dst_plan_buf = torch.zeros(x.runs_plan_bytes(self.dst_table), dtype=torch.uint8, device=dev)
         self.dst_plan = x.runs_prepare(self.dst_table, [(self.dst.data_ptr(), self.dst.numel())], True,
                                        self.dst_plan_buf)
+        self.f32wire = f32wire
+        if f32wire:
+            # BF16 results of the F32-wire sum: the drafter's 20 rows, and the whole partials
+            self.wire_rows = 20
+            self.out_rows = torch.zeros(self.wire_rows * HIDDEN, dtype=torch.int16, device=dev)
+            self.out_all = torch.zeros(n, dtype=torch.int16, device=dev)
         self.streamed = streamed
         if streamed:
             # both ranks' rings and results, and four default-priority streams
@@ -186,6 +192,11 @@ class Workload:
         ra, rb = self.ring_a, self.ring_b
         if self.streamed:
             return [("allreduce2_streamed", self._allreduce)]
+        if self.f32wire:
+            m = self.wire_rows * HIDDEN
+            return [("combine_f32wire_20x5120", lambda: x.combine2_f32(self.a[:m], self.b[:m], self.out_rows,
+                                                                      x.OUT_BF16)),
+                    ("combine_f32wire_full", lambda: x.combine2_f32(self.a, self.b, self.out_all, x.OUT_BF16))]
         ks = [
             ("pack_rank0", lambda: x.pack_bf16(self.a, ra, CHUNK, 0, nc)),
             ("pack_rank1", lambda: x.pack_bf16(self.b, rb, CHUNK, 0, nc)),
@@ -206,6 +217,9 @@ class Workload:
         if self.streamed:
             # per rank: pack 6 B, wire copy 2 B read + 2 B written, combine F32 8 B per element
             return {"allreduce2_streamed": 2 * 18 * self.n}
+        if self.f32wire:
+            # 4 + 4 B read, 2 B written per element
+            return {"combine_f32wire_20x5120": 10 * self.wire_rows * HIDDEN, "combine_f32wire_full": 10 * self.n}
         extra = (("gather_per_segment",) if self.seg_plan is not None else ()) + \
             (("fetch_coalesced",) if self.fetch_plan is not None else ())
         ab = algorithmic_bytes(self.tokens, extra)
@@ -322,6 +336,13 @@ WORKLOADS = {
                     "set by 72 dense-group descriptors (at most 32 MiB each) into one slab",
         "roofline_kernel": ("fetch_coalesced", "copy_descs (72 dense-group reads)", "descs_copy.hip",
                             "fetch_dense"),
+    },
+    "f32wire": {
+        "args": {"tokens": 16384, "shuffled": False, "f32wire": True},
+        "describe": "F32-wire all-reduce combine (two F32 partials summed in F32, rounded to BF16): the drafter's "
+                    "20 x 5120 rows, and 16384 x 5120",
+        "roofline_kernel": ("combine_f32wire_full", "combine2_f32 BF16 out (16384 x 5120)", "pack_combine.hip",
+                            "combine_f32wire_16384x5120"),
     },
     "streamed": {
         "args": {"tokens": TOKENS, "shuffled": False, "streamed": True},

@@ -24,7 +24,7 @@ OUT_F32, OUT_BF16 = 0, 1
 ARGMAX, TOP2 = 0, 1
 
 EXPORTED = [
-    "xfer_status_str", "xfer_pack_bf16", "xfer_combine2", "xfer_argmax_workspace_bytes",
+    "xfer_status_str", "xfer_pack_bf16", "xfer_combine2", "xfer_combine2_f32", "xfer_argmax_workspace_bytes",
     "xfer_argmax_merge", "xfer_runs_encode", "xfer_runs_validate", "xfer_runs_plan_bytes",
     "xfer_runs_prepare", "xfer_gather_runs", "xfer_scatter_runs", "xfer_allreduce2_event_id",
     "xfer_allreduce2_schedule", "xfer_events_create", "xfer_events_destroy", "xfer_allreduce2_streamed",
@@ -100,6 +100,8 @@ def lib():
         L.xfer_pack_bf16.restype = I
         L.xfer_combine2.argtypes = [P, P, S, P, I, P]
         L.xfer_combine2.restype = I
+        L.xfer_combine2_f32.argtypes = [P, P, S, P, I, P]
+        L.xfer_combine2_f32.restype = I
         L.xfer_argmax_workspace_bytes.argtypes = [U32, U32, U32]
         L.xfer_argmax_workspace_bytes.restype = S
         L.xfer_argmax_merge.argtypes = [ctypes.POINTER(Shard), ctypes.POINTER(Shard), I, P, P, S, P]
@@ -195,6 +197,22 @@ def combine2(a, b, out, mode: int, stream=None) -> None:
 
 def combine2_raw(a_ptr: int, b_ptr: int, n: int, out_ptr: int, mode: int, stream=None) -> int:
     return lib().xfer_combine2(a_ptr, b_ptr, n, out_ptr, mode, _stream(stream))
+
+
+def combine2_f32(a, b, out, mode: int, stream=None) -> None:
+    """F32-wire combine: a, b F32 CUDA tensors; out F32 (mode 0) or 2-byte (mode 1)."""
+    n = a.numel()
+    if b.numel() != n or out.numel() != n:
+        raise ValueError("size mismatch")
+    if a.element_size() != 4 or b.element_size() != 4:
+        raise ValueError("inputs must be 4-byte elements (F32)")
+    if out.element_size() != (4 if mode == OUT_F32 else 2):
+        raise ValueError("output element size does not match the mode")
+    _check(lib().xfer_combine2_f32(_dev(a), _dev(b), n, _dev(out), mode, _stream(stream)), "xfer_combine2_f32")
+
+
+def combine2_f32_raw(a_ptr: int, b_ptr: int, n: int, out_ptr: int, mode: int, stream=None) -> int:
+    return lib().xfer_combine2_f32(a_ptr, b_ptr, n, out_ptr, mode, _stream(stream))
 
 
 # ------------------------------------------------------------------- argmax

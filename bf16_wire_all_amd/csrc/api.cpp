@@ -255,6 +255,23 @@ int xfer_combine2(const uint16_t *a, const uint16_t *b, size_t n, void *out, int
   return XFER_OK;
 }
 
+int xfer_combine2_f32(const float *a, const float *b, size_t n, void *out, int out_mode, hipStream_t stream) {
+  if (out_mode != XFER_OUT_F32 && out_mode != XFER_OUT_BF16) return XFER_E_INVAL;
+  if (n == 0) return XFER_OK;
+  if (!a || !b || !out || !aligned16(a) || !aligned16(b) || !aligned16(out)) return XFER_E_INVAL;
+  if (n > SIZE_MAX / 4) return XFER_E_INVAL;
+  if (n > xfer::kMaxStreamElems) return XFER_E_UNSUPPORTED;
+  const uint64_t in_bytes = (uint64_t)n * 4;
+  const uint64_t out_bytes = (uint64_t)n * (out_mode == XFER_OUT_F32 ? 4 : 2);
+  const uintptr_t o = (uintptr_t)out;
+  for (const void *in : {(const void *)a, (const void *)b}) {
+    if (out_mode == XFER_OUT_F32 && in == (const void *)out) continue;  // in place: same element, same width
+    if (overlaps(o, out_bytes, (uintptr_t)in, in_bytes)) return XFER_E_INVAL;
+  }
+  if (xfer::launch_combine_f32(a, b, n, out, out_mode, stream) != hipSuccess) return XFER_E_DEVICE;
+  return XFER_OK;
+}
+
 size_t xfer_argmax_workspace_bytes(uint32_t rows, uint32_t ncols0, uint32_t ncols1) {
   return (size_t)xfer::argmax_workspace_bytes(rows, xfer::argmax_splits(rows, ncols0, ncols1));
 }

@@ -38,6 +38,7 @@ hipError_t launch_pack(const float *src, uint64_t n_elems, uint16_t *ring, uint6
                        uint64_t slot0_elem, hipStream_t stream);
 hipError_t launch_combine(const uint16_t *a, const uint16_t *b, uint64_t n, void *out, int mode,
                           hipStream_t stream);
+hipError_t launch_combine_f32(const float *a, const float *b, uint64_t n, void *out, int mode, hipStream_t stream);
 
 // ---- argmax (argmax.hip)
 struct ArgmaxShard {

@@ -140,6 +140,48 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const uint2 *a, const
   }
 }
 
+// F32-wire variant: both operands are F32 (12 B per element with F32 out,
+// 10 B with BF16 out), same chunking as the BF16-wire combine.
+__device__ __forceinline__ uint32_t sum_f32(uint32_t a, uint32_t b) {
+  const uint32_t s = __float_as_uint(__fadd_rn(__uint_as_float(a), __uint_as_float(b)));
+  return ((s & 0x7FFFFFFFu) > 0x7F800000u) ? 0x7FC00000u : s;
+}
+
+template <int MODE>
+__device__ __forceinline__ void combine_f32_quad(const uint4 *a, const uint4 *b, void *out, uint64_t q) {
+  const uint4 x = ld(&a[q]), y = ld(&b[q]);
+  uint4 s;
+  s.x = sum_f32(x.x, y.x);
+  s.y = sum_f32(x.y, y.y);
+  s.z = sum_f32(x.z, y.z);
+  s.w = sum_f32(x.w, y.w);
+  if (MODE == XFER_OUT_F32)
+    st(&reinterpret_cast<uint4 *>(out)[q], s);
+  else
+    st(&reinterpret_cast<uint2 *>(out)[q], pack_quad(s));
+}
+
+// In F32 mode out may be a or b itself (each thread reads its quads before
+// writing them); in BF16 mode out overlaps neither (host check).
+template <int MODE>
+__global__ __launch_bounds__(kThreads) void combine_f32_kernel(const uint4 *a, const uint4 *b, void *out,
+                                                               uint64_t n_quads, uint32_t tail) {
+  if (blockIdx.x == 0 && threadIdx.x < tail) {
+    const uint64_t e = n_quads * 4 + threadIdx.x;
+    const uint32_t s = sum_f32(reinterpret_cast<const uint32_t *>(a)[e], reinterpret_cast<const uint32_t *>(b)[e]);
+    if (MODE == XFER_OUT_F32)
+      reinterpret_cast<uint32_t *>(out)[e] = s;
+    else
+      reinterpret_cast<uint16_t *>(out)[e] = (uint16_t)bf16_rne(s);
+  }
+  const uint64_t q0 = (uint64_t)blockIdx.x * kQuadsPerBlock + threadIdx.x;
+#pragma unroll
+  for (int u = 0; u < kQuadsPerThread; ++u) {
+    const uint64_t q = q0 + u * kThreads;
+    if (q < n_quads) combine_f32_quad<MODE>(a, b, out, q);
+  }
+}
+
 // One workgroup per chunk of kQuadsPerBlock quads (at least one, for the tail).
 uint32_t grid_for(uint64_t n_quads) {
   const uint64_t g = (n_quads + kQuadsPerBlock - 1) / kQuadsPerBlock;
@@ -167,6 +209,17 @@ hipError_t launch_combine(const uint16_t *a, const uint16_t *b, uint64_t n, void
   if (mode == XFER_OUT_F32)
     return launch(combine_kernel<XFER_OUT_F32>, grid, dim3(kThreads), 0, stream, a2, b2, out, n_quads, tail);
   return launch(combine_kernel<XFER_OUT_BF16>, grid, dim3(kThreads), 0, stream, a2, b2, out, n_quads, tail);
+}
+
+hipError_t launch_combine_f32(const float *a, const float *b, uint64_t n, void *out, int mode, hipStream_t stream) {
+  const uint64_t n_quads = n / 4;
+  const uint32_t tail = (uint32_t)(n % 4);
+  const uint4 *a4 = reinterpret_cast<const uint4 *>(a);
+  const uint4 *b4 = reinterpret_cast<const uint4 *>(b);
+  const dim3 grid(grid_for(n_quads));
+  if (mode == XFER_OUT_F32)
+    return launch(combine_f32_kernel<XFER_OUT_F32>, grid, dim3(kThreads), 0, stream, a4, b4, out, n_quads, tail);
+  return launch(combine_f32_kernel<XFER_OUT_BF16>, grid, dim3(kThreads), 0, stream, a4, b4, out, n_quads, tail);
 }
 
 }  // namespace xfer

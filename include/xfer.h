@@ -119,6 +119,28 @@ enum { XFER_OUT_F32 = 0, XFER_OUT_BF16 = 1 };
 XFER_API int xfer_combine2(const uint16_t *a_rank0, const uint16_t *b_rank1, size_t n, void *out, int out_mode,
                   hipStream_t stream);
 
+/*
+ * xfer_combine2_f32 - the F32-wire all-reduce of [TP2] "Layout" and
+ * "Collectives" (the drafter's partials are pushed as F32, not BF16):
+ * out[i] = a[i] + b[i], one IEEE binary32 addition with rank 0's value first
+ * (so both ranks get identical bits), written as F32 (XFER_OUT_F32) or as
+ * that F32 sum rounded to BF16 with round to nearest even (XFER_OUT_BF16,
+ * the page's "fp32 sums rounded to bf16": two roundings, in that order).
+ *
+ *   a_rank0, b_rank1  (device) F32[n] each.
+ *   out               (device) F32[n] or BF16[n] bit patterns.
+ *
+ * Subnormals are kept; a NaN sum is written as 0x7FC00000 (F32) or 0x7FC0
+ * (BF16).
+ *
+ * Errors: XFER_E_INVAL for NULL or misaligned (16-byte) pointers, an unknown
+ * out_mode, or an output overlapping an input (except out == a_rank0 or
+ * out == b_rank1 exactly in F32 mode, computed in place);
+ * XFER_E_UNSUPPORTED for n above (2^24 - 1) * 2048 (one launch).
+ */
+XFER_API int xfer_combine2_f32(const float *a_rank0, const float *b_rank1, size_t n, void *out, int out_mode,
+                               hipStream_t stream);
+
 /* ------------------------------------------------------------ argmax merge */
 
 enum { XFER_ARGMAX = 0, XFER_TOP2 = 1 };

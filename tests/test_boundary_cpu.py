@@ -25,7 +25,7 @@ def _declared():
 
 def test_library_exports_every_declared_call():
     names = _declared()
-    assert len(names) == 20
+    assert len(names) == 21
     assert set(names) == set(x.EXPORTED)
     L = x.lib()
     for n in names:
@@ -71,6 +71,21 @@ def test_combine_argument_checks():
     assert f(a, b, 10, a, 0) == x.E_INVAL                         # F32 out cannot alias a
     assert f(a, b, 1000, b - 16, 1) == x.E_INVAL                  # BF16 out overlaps b partly
     assert f(a, a + 16, 10, a, 1) == x.E_INVAL                    # in place, but b overlaps out
+
+
+def test_combine_f32_argument_checks():
+    f = lambda *a: x.combine2_f32_raw(*a, stream=S0)
+    a, b, o = 0x100000, 0x200000, 0x300000
+    assert f(a, b, 10, o, 2) == x.E_INVAL                         # unknown mode
+    assert f(a, b, 0, o, 0) == x.OK                               # empty
+    assert f(0, b, 10, o, 0) == x.E_INVAL
+    assert f(a, b, 10, 0, 1) == x.E_INVAL
+    assert f(a + 8, b, 10, o, 0) == x.E_INVAL                     # misaligned
+    assert f(a, b, 10, a + 16, 0) == x.E_INVAL                    # F32 out overlaps a partly
+    assert f(a, b, 10, a, 1) == x.E_INVAL                         # BF16 out cannot alias a (other width)
+    assert f(a, b, 1000, b - 16, 0) == x.E_INVAL                  # overlaps b partly
+    assert f(a, a + 16, 10, a, 0) == x.E_INVAL                    # in place, but b overlaps out
+    assert f(a, b, ((1 << 24) - 1) * 2048 + 4, 1 << 40, 0) == x.E_UNSUPPORTED
 
 
 # ------------------------------------------------------------------ argmax
