@@ -72,6 +72,9 @@ def lib():
         L.oracle_groups_plan.restype = I
         L.oracle_copy_descs.argtypes = [P, U64, ctypes.POINTER(Region), I, P, U64]
         L.oracle_copy_descs.restype = I
+        L.oracle_paged_copy.argtypes = [U64, ctypes.POINTER(Region), P, U64, U64, ctypes.POINTER(Region), P, U64, U64,
+                                        U64]
+        L.oracle_paged_copy.restype = I
         _lib = L
     return _lib
 
@@ -261,3 +264,20 @@ def copy_descs(descs: np.ndarray, regions, slab: np.ndarray) -> None:
     reg = _regions(regions)
     _check(lib().oracle_copy_descs(_p(d) if d.size else None, d.size, reg, len(regions), _p(slab), slab.nbytes),
            "copy_descs")
+
+
+# -------------------------------------------------------------- paged copy
+
+def paged_copy(page_len: int, src_host: np.ndarray, src_idx, src_stride: int, src_offset: int,
+               dst_host: np.ndarray, dst_idx, dst_stride: int, dst_offset: int) -> None:
+    """Copy page src_idx[k] of src_host to page dst_idx[k] of dst_host (in place
+    on dst_host); page i of a list is at offset + i * stride."""
+    si = np.ascontiguousarray(src_idx, dtype=np.uint32)
+    di = np.ascontiguousarray(dst_idx, dtype=np.uint32)
+    assert si.size == di.size
+    assert src_host.dtype == np.uint8 and dst_host.dtype == np.uint8
+    s = Region(0, src_host.nbytes, src_host.ctypes.data)
+    d = Region(0, dst_host.nbytes, dst_host.ctypes.data)
+    _check(lib().oracle_paged_copy(page_len, ctypes.byref(s), _p(si) if si.size else None, src_stride, src_offset,
+                                   ctypes.byref(d), _p(di) if di.size else None, dst_stride, dst_offset, si.size),
+           "paged_copy")

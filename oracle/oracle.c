@@ -632,3 +632,63 @@ int oracle_copy_descs(const oracle_desc *descs, uint64_t n_descs, const oracle_r
   }
   return ORACLE_OK;
 }
+
+/* -------------------------------------------------------------- paged copy */
+
+/* Byte offset of page idx of a list inside a region of region_bytes, or -1
+ * if the page does not lie wholly inside it (checked arithmetic). */
+static int page_offset(uint32_t idx, uint64_t stride, uint64_t offset, uint64_t page_len, uint64_t region_bytes,
+                       uint64_t *out) {
+  if (stride && idx > (UINT64_MAX - offset) / stride) return -1;
+  const uint64_t at = offset + (uint64_t)idx * stride;
+  if (at > region_bytes || region_bytes - at < page_len) return -1;
+  *out = at;
+  return 0;
+}
+
+static int cmp_u64(const void *x, const void *y) {
+  const uint64_t a = *(const uint64_t *)x, b = *(const uint64_t *)y;
+  return a < b ? -1 : a > b;
+}
+
+/*
+ * [TE] the paged writes of the TransferEngine API: a page list is a set of
+ * page indices with one stride and one offset inside a registered region;
+ * page k of a list lies at region base + offset + indices[k] * stride, and
+ * the k-th source page is written to the k-th destination page, page_len
+ * bytes each (the page fixes only that pages are named by indices, a stride
+ * and an offset; this is the plainest reading).  Done here as data movement
+ * between two regions of one memory.  Every page must lie inside its region
+ * (ORACLE_ERANGE); destination pages must not overlap (ORACLE_EARG), so the
+ * order of the copies cannot matter.
+ */
+int oracle_paged_copy(uint64_t page_len, const oracle_region *src, const uint32_t *src_idx, uint64_t src_stride,
+                      uint64_t src_offset, const oracle_region *dst, const uint32_t *dst_idx, uint64_t dst_stride,
+                      uint64_t dst_offset, uint64_t n_pages) {
+  if (page_len == 0 || !src || !dst) return ORACLE_EARG;
+  if (n_pages == 0) return ORACLE_OK;
+  uint64_t *starts = malloc(n_pages * sizeof(uint64_t));
+  if (!starts) return ORACLE_EARG;
+  int rc = ORACLE_OK;
+  for (uint64_t k = 0; k < n_pages && rc == ORACLE_OK; ++k) {
+    uint64_t s = 0, d = 0;
+    if (page_offset(src_idx[k], src_stride, src_offset, page_len, src->bytes, &s) ||
+        page_offset(dst_idx[k], dst_stride, dst_offset, page_len, dst->bytes, &d))
+      rc = ORACLE_ERANGE;
+    starts[k] = d;
+  }
+  if (rc == ORACLE_OK) {
+    qsort(starts, n_pages, sizeof(uint64_t), cmp_u64);
+    for (uint64_t k = 1; k < n_pages; ++k)
+      if (starts[k] - starts[k - 1] < page_len) rc = ORACLE_EARG;
+  }
+  free(starts);
+  if (rc != ORACLE_OK) return rc;
+  for (uint64_t k = 0; k < n_pages; ++k) {
+    uint64_t s = 0, d = 0;
+    page_offset(src_idx[k], src_stride, src_offset, page_len, src->bytes, &s);
+    page_offset(dst_idx[k], dst_stride, dst_offset, page_len, dst->bytes, &d);
+    memcpy(dst->host + d, src->host + s, page_len);
+  }
+  return ORACLE_OK;
+}

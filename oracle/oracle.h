@@ -123,6 +123,13 @@ int oracle_groups_plan(const uint32_t *runs_per_lane, const uint64_t *run_base, 
 int oracle_copy_descs(const oracle_desc *descs, uint64_t n_descs, const oracle_region *regions, int n_regions,
                       uint8_t *slab, uint64_t slab_bytes);
 
+/* [TE] paged writes: dst page dst_idx[k] <- src page src_idx[k], page_len
+ * bytes, page i of a list at region start + offset + i * stride (offsets
+ * relative to each region's host image). */
+int oracle_paged_copy(uint64_t page_len, const oracle_region *src, const uint32_t *src_idx, uint64_t src_stride,
+                      uint64_t src_offset, const oracle_region *dst, const uint32_t *dst_idx, uint64_t dst_stride,
+                      uint64_t dst_offset, uint64_t n_pages);
+
 #ifdef __cplusplus
 }
 #endif
