@@ -84,7 +84,7 @@ class Workload:
     table, and a second table with one run per segment, are both gathered)."""
 
     def __init__(self, dev, tokens=TOKENS, shuffled=False, n_blocks=N_BLOCKS, seg=SEG, coalesced=False,
-                 streamed=False, f32wire=False):
+                 streamed=False, f32wire=False, paged=False):
         import numpy as np
         import torch
 
@@ -156,6 +156,30 @@ class Workload:
         self.dst_plan_buf = torch.zeros(x.runs_plan_bytes(self.dst_table), dtype=torch.uint8, device=dev)
         self.dst_plan = x.runs_prepare(self.dst_table, [(self.dst.data_ptr(), self.dst.numel())], True,
                                        self.dst_plan_buf)
+        self.paged = paged
+        if paged:
+            # the same set as Pages lists: per region, its lanes' pages -> block-major staging pages;
+            # then staging pages -> the slot-major destination (gap page per slot)
+            L, S = 2 * N_SLOTS, N_SLOTS // 2
+            pos_ = pos if pos is not None else np.arange(B, dtype=np.uint32)
+            bb = np.repeat(np.arange(B, dtype=np.int64), 2 * S)
+            jj = np.tile(np.arange(2 * S, dtype=np.int64), B)
+            self.page_plans, self.page_bufs = [], []
+            for r in range(2):
+                si = (pos_.astype(np.int64)[bb] * 2 * S + jj).astype(np.uint32)
+                di = (bb * L + r * 2 * S + jj).astype(np.uint32)
+                buf = torch.zeros(x.pages_plan_bytes(si.size), dtype=torch.uint8, device=dev)
+                self.page_plans.append(x.pages_prepare(SG, (bases[r], rb), si, SG, 0,
+                                                       (self.staging.data_ptr(), self.staging.numel()), di, SG, 0,
+                                                       buf))
+                self.page_bufs.append(buf)
+            k = np.arange(B * L, dtype=np.int64)
+            di = (((k // L) * N_SLOTS + (k % L) // 2) * 3 + (k % L) % 2).astype(np.uint32)
+            buf = torch.zeros(x.pages_plan_bytes(k.size), dtype=torch.uint8, device=dev)
+            self.page_scatter = x.pages_prepare(SG, (self.staging.data_ptr(), self.staging.numel()),
+                                                k.astype(np.uint32), SG, 0, (self.dst.data_ptr(), self.dst.numel()),
+                                                di, SG, 0, buf)
+            self.page_bufs.append(buf)
         self.f32wire = f32wire
         if f32wire:
             # BF16 results of the F32-wire sum: the drafter's 20 rows, and the whole partials
@@ -192,6 +216,10 @@ class Workload:
         ra, rb = self.ring_a, self.ring_b
         if self.streamed:
             return [("allreduce2_streamed", self._allreduce)]
+        if self.paged:
+            return [("paged_gather_region0", lambda: x.paged_copy(self.page_plans[0])),
+                    ("paged_gather_region1", lambda: x.paged_copy(self.page_plans[1])),
+                    ("paged_scatter", lambda: x.paged_copy(self.page_scatter))]
         if self.f32wire:
             m = self.wire_rows * HIDDEN
             return [("combine_f32wire_20x5120", lambda: x.combine2_f32(self.a[:m], self.b[:m], self.out_rows,
@@ -217,6 +245,9 @@ class Workload:
         if self.streamed:
             # per rank: pack 6 B, wire copy 2 B read + 2 B written, combine F32 8 B per element
             return {"allreduce2_streamed": 2 * 18 * self.n}
+        if self.paged:
+            kv = self.n_blocks * N_SLOTS * 2 * self.seg
+            return {"paged_gather_region0": kv, "paged_gather_region1": kv, "paged_scatter": 2 * kv}
         if self.f32wire:
             # 4 + 4 B read, 2 B written per element
             return {"combine_f32wire_20x5120": 10 * self.wire_rows * HIDDEN, "combine_f32wire_full": 10 * self.n}
@@ -336,6 +367,14 @@ WORKLOADS = {
                     "set by 72 dense-group descriptors (at most 32 MiB each) into one slab",
         "roofline_kernel": ("fetch_coalesced", "copy_descs (72 dense-group reads)", "descs_copy.hip",
                             "fetch_dense"),
+    },
+    "paged": {
+        "args": {"tokens": TOKENS, "shuffled": False, "paged": True},
+        "describe": "paged copy by Pages lists (indices, stride, offset): the 1000 x 288 x 2 x 4 KiB set gathered by "
+                    "two lists of 288,000 pages (one per region) into block-major staging, then scattered by one list "
+                    "of 576,000 pages into the 12 KiB slot-stride destination",
+        "roofline_kernel": ("paged_scatter", "paged_copy (576,000 pages of 4 KiB)", "pages_copy.hip",
+                            "paged_scatter"),
     },
     "f32wire": {
         "args": {"tokens": 16384, "shuffled": False, "f32wire": True},

@@ -29,6 +29,7 @@ EXPORTED = [
     "xfer_runs_prepare", "xfer_gather_runs", "xfer_scatter_runs", "xfer_allreduce2_event_id",
     "xfer_allreduce2_schedule", "xfer_events_create", "xfer_events_destroy", "xfer_allreduce2_streamed",
     "xfer_groups_plan", "xfer_descs_plan_bytes", "xfer_descs_prepare", "xfer_copy_descs",
+    "xfer_pages_plan_bytes", "xfer_pages_prepare", "xfer_paged_copy",
 ]
 
 
@@ -67,6 +68,17 @@ class DescsPlan(ctypes.Structure):
                 ("slab_bytes", ctypes.c_uint64), ("src_lo", ctypes.c_uint64), ("src_hi", ctypes.c_uint64),
                 ("max_pieces", ctypes.c_uint32), ("piece_bytes", ctypes.c_uint32), ("magic", ctypes.c_uint32),
                 ("reserved", ctypes.c_uint32)]
+
+
+class PagesC(ctypes.Structure):
+    _fields_ = [("indices", ctypes.c_void_p), ("stride", ctypes.c_uint64), ("offset", ctypes.c_uint64)]
+
+
+class PagesPlan(ctypes.Structure):
+    _fields_ = [("dev", ctypes.c_void_p), ("dev_bytes", ctypes.c_size_t), ("n_pages", ctypes.c_uint64),
+                ("page_len", ctypes.c_uint64), ("src_base", ctypes.c_uint64), ("src_stride", ctypes.c_uint64),
+                ("dst_base", ctypes.c_uint64), ("dst_stride", ctypes.c_uint64), ("off_src_idx", ctypes.c_uint64),
+                ("off_dst_idx", ctypes.c_uint64), ("units_per_page", ctypes.c_uint32), ("magic", ctypes.c_uint32)]
 
 
 class Region(ctypes.Structure):
@@ -139,6 +151,13 @@ def lib():
         L.xfer_descs_prepare.restype = I
         L.xfer_copy_descs.argtypes = [ctypes.POINTER(DescsPlan), P, S, P]
         L.xfer_copy_descs.restype = I
+        L.xfer_pages_plan_bytes.argtypes = [U64]
+        L.xfer_pages_plan_bytes.restype = S
+        L.xfer_pages_prepare.argtypes = [U64, ctypes.POINTER(Region), ctypes.POINTER(PagesC), ctypes.POINTER(Region),
+                                         ctypes.POINTER(PagesC), U64, P, S, ctypes.POINTER(PagesPlan)]
+        L.xfer_pages_prepare.restype = I
+        L.xfer_paged_copy.argtypes = [ctypes.POINTER(PagesPlan), P]
+        L.xfer_paged_copy.restype = I
         _lib = L
     return _lib
 
@@ -476,3 +495,37 @@ def descs_prepare(descs: np.ndarray, slab_bytes: int, regions, dev) -> DescsPlan
 def copy_descs(plan: DescsPlan, slab, stream=None) -> None:
     _check(lib().xfer_copy_descs(ctypes.byref(plan), _dev(slab), slab.numel() * slab.element_size(),
                                  _stream(stream)), "xfer_copy_descs")
+
+
+# ------------------------------------------------------ paged copy (Pages)
+
+def pages_plan_bytes(n_pages: int) -> int:
+    return int(lib().xfer_pages_plan_bytes(n_pages))
+
+
+def pages_prepare_status(page_len: int, src_region, src_idx, src_stride: int, src_offset: int, dst_region, dst_idx,
+                         dst_stride: int, dst_offset: int, dev_ptr: int, dev_bytes: int):
+    """src_region, dst_region: (device base, bytes); *_idx: page indices (host)."""
+    si = np.ascontiguousarray(src_idx, dtype=np.uint32)
+    di = np.ascontiguousarray(dst_idx, dtype=np.uint32)
+    if si.size != di.size:
+        raise ValueError("page lists differ in length")
+    sr, dr = Region(*src_region), Region(*dst_region)
+    sp = PagesC(si.ctypes.data if si.size else None, src_stride, src_offset)
+    dp = PagesC(di.ctypes.data if di.size else None, dst_stride, dst_offset)
+    plan = PagesPlan()
+    st = lib().xfer_pages_prepare(page_len, ctypes.byref(sr), ctypes.byref(sp), ctypes.byref(dr), ctypes.byref(dp),
+                                  si.size, dev_ptr, dev_bytes, ctypes.byref(plan))
+    return st, plan
+
+
+def pages_prepare(page_len: int, src_region, src_idx, src_stride: int, src_offset: int, dst_region, dst_idx,
+                  dst_stride: int, dst_offset: int, dev) -> PagesPlan:
+    st, plan = pages_prepare_status(page_len, src_region, src_idx, src_stride, src_offset, dst_region, dst_idx,
+                                    dst_stride, dst_offset, _dev(dev), dev.numel() * dev.element_size())
+    _check(st, "xfer_pages_prepare")
+    return plan
+
+
+def paged_copy(plan: PagesPlan, stream=None) -> None:
+    _check(lib().xfer_paged_copy(ctypes.byref(plan), _stream(stream)), "xfer_paged_copy")

@@ -10,7 +10,7 @@ BUILD = os.path.join(ROOT, "_build", "xfer")
 LIB = os.path.join(HERE, "libxfer.so")
 
 SOURCES = ["api.cpp", "stream_pipeline.cpp", "groups.cpp", "pack_combine.hip", "argmax.hip", "runs_copy.hip",
-           "descs_copy.hip"]
+           "descs_copy.hip", "pages.cpp", "pages_copy.hip"]
 
 # -packed-fp32-ops: never emit packed F32 instructions (the host pass warns
 # that it does not know the feature; harmless).  No fast-math and no denormal

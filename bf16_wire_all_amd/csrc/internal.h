@@ -28,6 +28,15 @@ constexpr uint64_t kMaxGridBlocks = (1ull << 24) - 1;
 // Pack and combine move 2048 elements per workgroup.
 constexpr uint64_t kMaxStreamElems = kMaxGridBlocks * 2048;
 
+// ---- paged copy (pages_copy.hip): 4 KiB units, two per workgroup
+constexpr uint32_t kPageUnitBytes = 4096;
+struct PagesView {
+  const uint32_t *src_idx, *dst_idx;
+  uint64_t src_base, src_stride, dst_base, dst_stride, page_len;
+  uint32_t units_per_page, n_units;
+};
+hipError_t launch_paged_copy(const PagesView &v, hipStream_t stream);
+
 // ---- host helpers shared by the entry points (api.cpp)
 int validate_table(const xfer_run_table *t, const xfer_region *regions, int n_regions, int is_dst,
                    uint64_t *span_lo, uint64_t *span_hi);

@@ -411,6 +411,68 @@ XFER_API int xfer_descs_prepare(const xfer_desc *descs, uint64_t n_descs, uint64
  */
 XFER_API int xfer_copy_descs(const xfer_descs_plan *plan, void *slab, size_t slab_bytes, hipStream_t stream);
 
+/* ------------------------------------------------ paged copy (Pages lists) */
+
+/*
+ * A page list of [TE] (the Pages type of the TransferEngine API, which its
+ * paged writes take for both ends): page k of the list lies at
+ * region base + offset + indices[k] * stride.  The page names pages only by
+ * indices, a stride and an offset; this is the plainest reading.
+ */
+typedef struct {
+  const uint32_t *indices; /* (host) one index per page                        */
+  uint64_t stride;         /* bytes per index step, multiple of 16             */
+  uint64_t offset;         /* bytes from the region base to index 0, mult. 16  */
+} xfer_pages;
+
+/* Filled by xfer_pages_prepare; the caller owns dev. */
+typedef struct {
+  void *dev;
+  size_t dev_bytes;
+  uint64_t n_pages, page_len;
+  uint64_t src_base, src_stride; /* region base + offset, and the stride */
+  uint64_t dst_base, dst_stride;
+  uint64_t off_src_idx, off_dst_idx; /* index arrays inside dev */
+  uint32_t units_per_page;           /* ceil(page_len / 4096)    */
+  uint32_t magic;
+} xfer_pages_plan;
+
+/* Device bytes xfer_pages_prepare needs for n_pages pages. */
+XFER_API size_t xfer_pages_plan_bytes(uint64_t n_pages);
+
+/*
+ * xfer_pages_prepare - check two page lists of n_pages pages each and upload
+ * their indices (blocking): source page k will be copied to destination page
+ * k, page_len bytes.  src and dst are the regions the lists address (their
+ * base is the device address of the region, 16-byte aligned).  Checks, in
+ * this order:
+ *   XFER_E_INVAL  NULL out, regions or page lists (with n_pages > 0), a
+ *                 page_len that is 0 or not a multiple of 16, a stride,
+ *                 offset or region base not a multiple of 16, a region that
+ *                 wraps past 2^64, or source and destination regions that
+ *                 overlap;
+ *   XFER_E_UNSUPPORTED  more than 2^32 - 1 units of 4 KiB, or a grid above
+ *                 2^24 - 1 workgroups;
+ *   XFER_E_RANGE  a page (either list) not wholly inside its region, or
+ *                 offset arithmetic that overflows 64 bits;
+ *   XFER_E_OVERLAP  two destination pages that overlap;
+ *   XFER_E_INVAL  dev NULL, misaligned or smaller than
+ *                 xfer_pages_plan_bytes(n_pages);
+ *   XFER_E_DEVICE  the upload failed.
+ */
+XFER_API int xfer_pages_prepare(uint64_t page_len, const xfer_region *src, const xfer_pages *src_pages,
+                                const xfer_region *dst, const xfer_pages *dst_pages, uint64_t n_pages, void *dev,
+                                size_t dev_bytes, xfer_pages_plan *out);
+
+/*
+ * xfer_paged_copy - [TE] paged writes done as data movement on one GPU: for
+ * every k, the page_len bytes of source page k are copied to destination
+ * page k.  A gather is a destination list of consecutive indices; a scatter
+ * a source list of consecutive indices.
+ * Errors: XFER_E_INVAL for a NULL or foreign plan.
+ */
+XFER_API int xfer_paged_copy(const xfer_pages_plan *plan, hipStream_t stream);
+
 /* -------------------------------------------- streamed two-rank all-reduce */
 
 /*

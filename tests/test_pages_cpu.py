@@ -115,3 +115,62 @@ def test_scatter_by_pages_places_every_page():
                 assert np.array_equal(dst[page:page + seg], staging[k * seg:(k + 1) * seg])
             gap = ((b * S + s) * 3 + 2) * seg
             assert np.all(dst[gap:gap + seg] == 0xA5)
+
+
+# ------------------------------------------------------ library host checks
+
+SRC = (0x10000000, 1 << 20)
+DST = (0x20000000, 1 << 20)
+
+
+def _prep(page_len=4096, si=(0, 1), ss=4096, so=0, di=(0, 1), ds=4096, do=0, src=SRC, dst=DST, dev=0, dev_bytes=0):
+    st, _ = x.pages_prepare_status(page_len, src, si, ss, so, dst, di, ds, do, dev, dev_bytes)
+    return st
+
+
+def test_library_checks_in_order():
+    assert _prep(page_len=0) == x.E_INVAL
+    assert _prep(page_len=24) == x.E_INVAL                                # not a multiple of 16
+    assert _prep(ss=4104) == x.E_INVAL                                    # misaligned stride
+    assert _prep(do=8) == x.E_INVAL                                       # misaligned offset
+    assert _prep(src=(0x10000008, 1 << 20)) == x.E_INVAL                  # misaligned region
+    assert _prep(dst=(0x10080000, 1 << 20)) == x.E_INVAL                  # regions overlap
+    assert _prep(si=(0, 256)) == x.E_RANGE                                # source page past the end
+    assert _prep(di=(255, 256)) == x.E_RANGE                              # destination page past the end
+    assert _prep(si=(0, 0xFFFFFFFF), ss=1 << 40) == x.E_RANGE             # offset arithmetic overflows
+    assert _prep(di=(0, 1), ds=2048) == x.E_OVERLAP                       # destination pages overlap
+    assert _prep(di=(3, 3)) == x.E_OVERLAP                                # the same page twice
+    assert _prep(si=(3, 3)) == x.E_INVAL                                  # same source page twice is fine: then no dev
+    assert _prep() == x.E_INVAL                                           # valid lists, no device buffer
+    assert _prep(si=(), di=()) == x.OK                                    # no pages: nothing to upload
+
+
+def test_library_refuses_oversized_launches():
+    n = 1 << 21                                                           # 2^21 pages of 64 KiB = 2^25 units
+    idx = np.arange(n, dtype=np.uint32)
+    big = (1 << 40, 1 << 38)
+    assert _prep(page_len=65536, si=idx, ss=65536, di=idx, ds=65536, src=big, dst=(1 << 41, 1 << 38)) == \
+        x.E_UNSUPPORTED
+    assert _prep(page_len=1 << 28, si=np.arange(1 << 16 | 1, dtype=np.uint32), ss=1 << 28,
+                 di=np.arange(1 << 16 | 1, dtype=np.uint32), ds=1 << 28, src=(1 << 44, 1 << 45),
+                 dst=(1 << 46, 1 << 45)) == x.E_UNSUPPORTED             # more than 2^32 - 1 units
+
+
+def test_library_agrees_with_oracle_on_what_is_refused():
+    """The same lists, refused or accepted alike by the oracle and the library."""
+    cases = [dict(si=(0, 256)), dict(di=(255, 256)), dict(di=(0, 1), ds=2048), dict(si=(0, 1))]
+    for c in cases:
+        st = _prep(**c)
+        src = np.zeros(SRC[1], np.uint8)
+        dst = np.zeros(DST[1], np.uint8)
+        try:
+            oracle.paged_copy(4096, src, c.get("si", (0, 1)), c.get("ss", 4096), 0, dst, c.get("di", (0, 1)),
+                              c.get("ds", 4096), 0)
+            ok = True
+        except oracle.OracleError:
+            ok = False
+        assert ok == (st == x.E_INVAL), (c, st)   # accepted lists fail only for the missing device buffer
+
+
+def test_paged_copy_refuses_foreign_plans():
+    assert x.lib().xfer_paged_copy(x.ctypes.byref(x.PagesPlan()), None) == x.E_INVAL
