@@ -71,6 +71,8 @@ SMALL = [
     (100, 6, 80, 4),       # 5 vectors per segment
     (31, 10, 1024, 5),
     (7, 2, 65536, 6),      # 64 KiB segments
+    (5, 2, 49168, 3),      # 3073 vectors: a large segment that is not a power of two
+    (3, 2, 1 << 20, None),  # the largest segment the plan accepts: 1 MiB, 128 pieces
 ]
 
 
