@@ -91,7 +91,7 @@ class RunsPlan(ctypes.Structure):
                 ("span_lo", ctypes.c_uint64), ("span_hi", ctypes.c_uint64), ("is_dst", ctypes.c_uint32),
                 ("tile_blocks", ctypes.c_uint32), ("n_tiles", ctypes.c_uint32), ("group_blocks", ctypes.c_uint32),
                 ("n_groups", ctypes.c_uint32), ("pieces", ctypes.c_uint32), ("magic", ctypes.c_uint32),
-                ("off_group_run", ctypes.c_uint64), ("off_run_start", ctypes.c_uint64),
+                ("lanes_per_wg", ctypes.c_uint32), ("off_group_run", ctypes.c_uint64), ("off_run_start", ctypes.c_uint64),
                 ("off_run_base", ctypes.c_uint64), ("off_run_stride", ctypes.c_uint64)]
 
 

@@ -68,7 +68,9 @@ struct PlanView {
   const uint64_t *run_base;   // [n_runs]
   const int64_t *run_stride;  // [n_runs]
   uint32_t n_lanes, n_blocks;
-  uint32_t tile_blocks;       // blocks per workgroup; divides group_blocks
+  uint32_t lanes_per_wg;      // 1 or 2: a workgroup copies lanes l and l + lane_slots
+  uint32_t lane_slots;        // ceil(n_lanes / lanes_per_wg)
+  uint32_t tile_blocks;       // blocks per workgroup and lane; divides group_blocks
   uint32_t n_tiles;           // per lane
   uint32_t group_blocks;      // blocks per index entry
   uint32_t n_groups;          // per lane
@@ -80,6 +82,7 @@ struct PlanView {
 };
 constexpr uint32_t kMaxGroupBlocks = 32;
 constexpr uint32_t kMaxTileBlocks = 32;
+constexpr uint32_t kMaxLanesPerWorkgroup = 2;
 constexpr uint32_t kMaxSegVectors = 1u << 16;  // 1 MiB segments
 hipError_t launch_gather(const PlanView &p, void *staging, hipStream_t stream);
 hipError_t launch_scatter(const PlanView &p, const void *staging, hipStream_t stream);

@@ -1,17 +1,20 @@
 // Gather / scatter of fixed-size segments addressed by a run-encoded table.
 //
-// Work unit: one workgroup per (lane l, tile of tile_blocks consecutive
-// blocks).  Consecutive workgroups take consecutive lanes of the same block
-// tile, so at any moment the chip is reading and writing a few neighbouring
-// address windows rather than scattered ones.  Tiles are small (2 blocks of
-// 4 KiB by default): many short workgroups, each moving 8 KiB in one pass,
-// kept HBM busier on MI355X than fewer long ones (measured 6.0-6.4 TB/s
-// against 5.2-5.4 TB/s for 32-block tiles).
+// Work unit: one workgroup per (lane slot, tile of tile_blocks consecutive
+// blocks), about 8 KiB in all.  A slot is one lane, or (lanes_per_wg = 2, for
+// tables whose lanes are broken into many runs) lane l and lane
+// l + ceil(L/2), 4 KiB each.  Large segments are cut into pieces, one
+// workgroup each.  Consecutive workgroups take consecutive slots of the same
+// block tile, so the chip reads and writes a few neighbouring address windows
+// at a time.  Measured on MI355X on the paged K/V set: many short workgroups
+// moving 8 KiB in one pass beat longer ones (32-block tiles: 5.2-5.4 TB/s);
+// the host picks one lane or two per workgroup by measurement (see the plan
+// layout).
 //
 // Decode, staged in LDS (no per-segment address table exists anywhere):
-//   1. the plan's group index (one entry per lane and group of 32 blocks)
-//      gives the first run covering the workgroup's group and, via the next
-//      entry, the last one: at most 33 runs, loaded in parallel into LDS;
+//   1. per lane, the plan's group index (one entry per lane and group of 32
+//      blocks) gives the first run covering the workgroup's group and, via the
+//      next entry, the last one: at most 33 runs, loaded in parallel into LDS;
 //   2. each block of the tile finds its run by binary search over the LDS
 //      run starts and computes addr = base + (b - start) * stride;
 //   3. the segment copies read those addresses from LDS (a wave mostly reads
@@ -58,47 +61,63 @@ __device__ __forceinline__ void split_index(uint32_t v, uint32_t w, uint32_t w_l
 template <bool GATHER, bool POW2>
 __global__ __launch_bounds__(kThreads) void runs_copy_kernel(PlanView p, uint8_t *staging_w,
                                                              const uint8_t *staging_r) {
-  __shared__ uint32_t s_start[kMaxGroupBlocks + 1];
-  __shared__ uint64_t s_base[kMaxGroupBlocks + 1];
-  __shared__ int64_t s_stride[kMaxGroupBlocks + 1];
-  __shared__ uint64_t s_addr[kMaxTileBlocks];
+  constexpr int LW = kMaxLanesPerWorkgroup;
+  constexpr int NR = kMaxGroupBlocks + 1;
+  __shared__ uint32_t s_start[LW][NR];
+  __shared__ uint64_t s_base[LW][NR];
+  __shared__ int64_t s_stride[LW][NR];
+  __shared__ uint64_t s_addr[LW][kMaxTileBlocks];
 
-  // Workgroup -> (piece, lane, tile), pieces fastest: consecutive workgroups
-  // stream consecutive pieces of one segment, then the next lane's.
+  // Workgroup -> (piece, lane slot, tile), pieces fastest: consecutive
+  // workgroups stream consecutive pieces of one segment, then the next slot's.
   const uint32_t piece = blockIdx.x % p.pieces;
   const uint32_t rest = blockIdx.x / p.pieces;
-  const uint32_t l = rest % p.n_lanes;
-  const uint32_t t = rest / p.n_lanes;
+  const uint32_t slot = rest % p.lane_slots;
+  const uint32_t t = rest / p.lane_slots;
   const uint32_t b0 = t * p.tile_blocks;
   const uint32_t nb = min(p.tile_blocks, p.n_blocks - b0);
   const uint32_t tid = threadIdx.x;
+  // Lanes of this workgroup: slot, and slot + lane_slots when it exists.
+  // slot < lane_slots <= n_lanes, so the first always does.
+  static_assert(LW == 2, "the decode below handles one or two lanes");
+  const uint32_t lane0 = slot, lane1 = slot + p.lane_slots;
+  const uint32_t n_here = (p.lanes_per_wg == 2 && lane1 < p.n_lanes) ? 2 : 1;
 
-  // Runs covering the tile's group of blocks (the tile lies inside one group).
+  // Runs covering the tile's group of blocks, per lane (the tile lies inside
+  // one group): at most group_blocks + 1 each.
   const uint32_t g = b0 / p.group_blocks;
-  const uint32_t *gr = p.group_run + (uint64_t)l * (p.n_groups + 1);
-  const uint32_t r0 = gr[g];
-  const uint32_t lane_end = gr[p.n_groups];
-  const uint32_t r1 = min(gr[g + 1] + 1, lane_end);
-  const uint32_t nr = r1 - r0;  // <= group_blocks + 1
-
-  for (uint32_t i = tid; i < nr; i += kThreads) {
-    s_start[i] = p.run_start[r0 + i];
-    s_base[i] = p.run_base[r0 + i];
-    s_stride[i] = p.run_stride[r0 + i];
+  const uint32_t *gr0 = p.group_run + (uint64_t)lane0 * (p.n_groups + 1);
+  const uint32_t ra = gr0[g];
+  const uint32_t na = min(gr0[g + 1] + 1, gr0[p.n_groups]) - ra;
+  uint32_t rb = 0, nbr = 0;
+  if (n_here == 2) {
+    const uint32_t *gr1 = p.group_run + (uint64_t)lane1 * (p.n_groups + 1);
+    rb = gr1[g];
+    nbr = min(gr1[g + 1] + 1, gr1[p.n_groups]) - rb;
+  }
+  for (uint32_t k = tid; k < na + nbr; k += kThreads) {
+    const bool second = k >= na;
+    const uint32_t m = second ? k - na : k;
+    const uint32_t r = (second ? rb : ra) + m;
+    const int i = second ? 1 : 0;
+    s_start[i][m] = p.run_start[r];
+    s_base[i][m] = p.run_base[r];
+    s_stride[i][m] = p.run_stride[r];
   }
   __syncthreads();
-  for (uint32_t j = tid; j < nb; j += kThreads) {
+  for (uint32_t k = tid; k < n_here * nb; k += kThreads) {
+    const uint32_t i = k / nb, j = k - i * nb;
     const uint32_t b = b0 + j;
-    // last run i with s_start[i] <= b; s_start[0] <= group start <= b
-    uint32_t lo = 0, hi = nr;
+    // last run m with s_start[i][m] <= b; s_start[i][0] <= group start <= b
+    uint32_t lo = 0, hi = i ? nbr : na;
     while (hi - lo > 1) {
       const uint32_t mid = (lo + hi) / 2;
-      if (s_start[mid] <= b)
+      if (s_start[i][mid] <= b)
         lo = mid;
       else
         hi = mid;
     }
-    s_addr[j] = s_base[lo] + (uint64_t)(b - s_start[lo]) * (uint64_t)s_stride[lo];
+    s_addr[i][j] = s_base[i][lo] + (uint64_t)(b - s_start[i][lo]) * (uint64_t)s_stride[i][lo];
   }
   __syncthreads();
 
@@ -106,41 +125,45 @@ __global__ __launch_bounds__(kThreads) void runs_copy_kernel(PlanView p, uint8_t
   const uint64_t v0 = (uint64_t)piece * w;  // first vector of this workgroup's piece
   const uint32_t total = nb * w;
   const uint64_t block_step = (uint64_t)p.n_lanes * p.seg_bytes;  // staging bytes between blocks
-  const uint8_t *stage0 = (GATHER ? (const uint8_t *)staging_w : staging_r) +
-                          ((uint64_t)b0 * p.n_lanes + l) * p.seg_bytes;
-
-  // Address of vector v on the staging side and on the table side.
-  auto stage_at = [&](uint32_t vv) {
-    uint32_t j, o;
-    split_index<POW2>(vv, w, p.piece_log2, j, o);
-    return (uint64_t)stage0 + j * block_step + 16ull * (v0 + o);
-  };
-  auto table_at = [&](uint32_t vv) {
-    uint32_t j, o;
-    split_index<POW2>(vv, w, p.piece_log2, j, o);
-    return s_addr[j] + 16ull * (v0 + o);
-  };
-  uint32_t v = tid;
-  for (; v + (kUnroll - 1) * kThreads < total; v += kUnroll * kThreads) {
-    v4u x[kUnroll];
+  for (uint32_t i = 0; i < n_here; ++i) {
+    const uint32_t l = i ? lane1 : lane0;
+    const uint8_t *stage0 = (GATHER ? (const uint8_t *)staging_w : staging_r) +
+                            ((uint64_t)b0 * p.n_lanes + l) * p.seg_bytes;
+    const uint64_t *addr = s_addr[i];
+    // Address of vector v on the staging side and on the table side.
+    auto stage_at = [&](uint32_t vv) {
+      uint32_t j, o;
+      split_index<POW2>(vv, w, p.piece_log2, j, o);
+      return (uint64_t)stage0 + j * block_step + 16ull * (v0 + o);
+    };
+    auto table_at = [&](uint32_t vv) {
+      uint32_t j, o;
+      split_index<POW2>(vv, w, p.piece_log2, j, o);
+      return addr[j] + 16ull * (v0 + o);
+    };
+    uint32_t v = tid;
+    for (; v + (kUnroll - 1) * kThreads < total; v += kUnroll * kThreads) {
+      v4u x[kUnroll];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const uint32_t vv = v + u * kThreads;
-      x[u] = load16(GATHER ? table_at(vv) : stage_at(vv));
-    }
+      for (int u = 0; u < kUnroll; ++u) {
+        const uint32_t vv = v + u * kThreads;
+        x[u] = load16(GATHER ? table_at(vv) : stage_at(vv));
+      }
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const uint32_t vv = v + u * kThreads;
-      store16(GATHER ? stage_at(vv) : table_at(vv), x[u]);
+      for (int u = 0; u < kUnroll; ++u) {
+        const uint32_t vv = v + u * kThreads;
+        store16(GATHER ? stage_at(vv) : table_at(vv), x[u]);
+      }
     }
+    for (; v < total; v += kThreads)
+      store16(GATHER ? stage_at(v) : table_at(v), load16(GATHER ? table_at(v) : stage_at(v)));
   }
-  for (; v < total; v += kThreads) store16(GATHER ? stage_at(v) : table_at(v), load16(GATHER ? table_at(v) : stage_at(v)));
 }
 
 }  // namespace
 
 hipError_t launch_gather(const PlanView &p, void *staging, hipStream_t stream) {
-  const dim3 grid(p.n_lanes * p.n_tiles * p.pieces);
+  const dim3 grid(p.lane_slots * p.n_tiles * p.pieces);
   uint8_t *w = reinterpret_cast<uint8_t *>(staging);
   if (p.piece_log2 < 32)
     return launch(runs_copy_kernel<true, true>, grid, dim3(kThreads), 0, stream, p, w, (const uint8_t *)w);
@@ -148,7 +171,7 @@ hipError_t launch_gather(const PlanView &p, void *staging, hipStream_t stream) {
 }
 
 hipError_t launch_scatter(const PlanView &p, const void *staging, hipStream_t stream) {
-  const dim3 grid(p.n_lanes * p.n_tiles * p.pieces);
+  const dim3 grid(p.lane_slots * p.n_tiles * p.pieces);
   const uint8_t *r = reinterpret_cast<const uint8_t *>(staging);
   if (p.piece_log2 < 32)
     return launch(runs_copy_kernel<false, true>, grid, dim3(kThreads), 0, stream, p, (uint8_t *)nullptr, r);

@@ -288,6 +288,7 @@ typedef struct {
   uint32_t n_groups;
   uint32_t pieces;
   uint32_t magic;
+  uint32_t lanes_per_wg;
   uint64_t off_group_run, off_run_start, off_run_base, off_run_stride;
 } xfer_runs_plan;
 

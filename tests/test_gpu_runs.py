@@ -230,3 +230,35 @@ def test_plan_misuse_refused():
     assert x.gather_runs_raw(plan, staging.data_ptr(), staging.numel() - 16) == x.E_INVAL  # small staging
     assert x.gather_runs_raw(plan, regs[0].data_ptr(), regs[0].numel()) == x.E_INVAL       # staging = source
     assert np.all(down(staging) == 0x11)
+
+
+def test_odd_lane_count_scattered_table():
+    """Five lanes of scattered single-segment runs (the host pairs lanes l and
+    l + 3 per workgroup; the last slot holds one lane), gathered and
+    scattered back to a mirror."""
+    n_lanes, n_blocks, seg = 5, 37, 272
+    region = zeros(n_lanes * n_blocks * seg + 4096)
+    base = region.data_ptr()
+    order = dg.permutation(n_lanes * n_blocks, 41)
+    a = (np.uint64(base) + order.astype(np.uint64).reshape(n_lanes, n_blocks) * np.uint64(seg))
+    host = np.empty(region.numel(), np.uint8)
+    dg.fill_region(host, base, a, seg, 43)
+    region.copy_(torch.from_numpy(host))
+    t = x.runs_encode(a, seg)
+    assert t.n_runs > 2 * n_lanes
+    plan, _b = _plan(t, [(base, region.numel())], False)
+    assert plan.lanes_per_wg == 2
+    staging = filled(n_lanes * n_blocks * seg + 64, 0x3C)
+    x.gather_runs(plan, staging)
+    want = oracle.gather(_otable(t), seg, [(base, host)])
+    got = down(staging)
+    assert np.array_equal(got[:want.size], want) and np.all(got[want.size:] == 0x3C)
+    mirror = filled(region.numel(), 0x5A)
+    ma = a - np.uint64(base) + np.uint64(mirror.data_ptr())
+    mt = x.runs_encode(ma, seg)
+    mplan, _mb = _plan(mt, [(mirror.data_ptr(), mirror.numel())], True)
+    assert mplan.lanes_per_wg == 2
+    x.scatter_runs(up(want), mplan)
+    mwant = np.full(mirror.numel(), 0x5A, np.uint8)
+    oracle.scatter(_otable(mt), seg, [(mirror.data_ptr(), mwant)], want)
+    assert np.array_equal(down(mirror), mwant)
