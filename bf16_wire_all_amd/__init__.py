@@ -30,6 +30,7 @@ EXPORTED = [
     "xfer_allreduce2_schedule", "xfer_events_create", "xfer_events_destroy", "xfer_allreduce2_streamed",
     "xfer_groups_plan", "xfer_descs_plan_bytes", "xfer_descs_prepare", "xfer_copy_descs",
     "xfer_pages_plan_bytes", "xfer_pages_prepare", "xfer_paged_copy",
+    "xfer_allreduce2_graph_create", "xfer_allreduce2_graph_launch", "xfer_allreduce2_graph_destroy",
 ]
 
 
@@ -151,6 +152,12 @@ def lib():
         L.xfer_descs_prepare.restype = I
         L.xfer_copy_descs.argtypes = [ctypes.POINTER(DescsPlan), P, S, P]
         L.xfer_copy_descs.restype = I
+        L.xfer_allreduce2_graph_create.argtypes = [ctypes.POINTER(AllReduce2Desc), ctypes.POINTER(ctypes.c_void_p)]
+        L.xfer_allreduce2_graph_create.restype = I
+        L.xfer_allreduce2_graph_launch.argtypes = [P, P]
+        L.xfer_allreduce2_graph_launch.restype = I
+        L.xfer_allreduce2_graph_destroy.argtypes = [P]
+        L.xfer_allreduce2_graph_destroy.restype = I
         L.xfer_pages_plan_bytes.argtypes = [U64]
         L.xfer_pages_plan_bytes.restype = S
         L.xfer_pages_prepare.argtypes = [U64, ctypes.POINTER(Region), ctypes.POINTER(PagesC), ctypes.POINTER(Region),
@@ -400,11 +407,11 @@ class Events:
             pass
 
 
-def allreduce2_streamed(src, send, recv, out, chunk_bytes: int, mode: int, compute, wire, events: Events,
-                        ring_bytes: int | None = None) -> int:
-    """src, send, recv, out: pairs of CUDA tensors (rank 0, rank 1); compute,
-    wire: pairs of torch streams (or raw stream handles).  Returns the status."""
+def _allreduce2_desc(src, send, recv, out, chunk_bytes: int, mode: int, compute=None, wire=None, events=None,
+                     ring_bytes: int | None = None) -> AllReduce2Desc:
     def h(s):
+        if s is None:
+            return None
         return s.cuda_stream if hasattr(s, "cuda_stream") else int(s)
     d = AllReduce2Desc()
     for r in range(2):
@@ -412,14 +419,56 @@ def allreduce2_streamed(src, send, recv, out, chunk_bytes: int, mode: int, compu
         d.send[r] = _dev(send[r])
         d.recv[r] = _dev(recv[r])
         d.out[r] = _dev(out[r])
-        d.compute[r] = h(compute[r])
-        d.wire[r] = h(wire[r])
+        d.compute[r] = h(compute[r]) if compute is not None else None
+        d.wire[r] = h(wire[r]) if wire is not None else None
     d.n = src[0].numel() * src[0].element_size() // 4     # F32 elements
     d.chunk_bytes = chunk_bytes
     d.ring_bytes = send[0].numel() * send[0].element_size() if ring_bytes is None else ring_bytes
     d.out_mode = mode
-    d.events = ctypes.cast(events.array, ctypes.c_void_p)
+    d.events = ctypes.cast(events.array, ctypes.c_void_p) if events is not None else None
+    return d
+
+
+def allreduce2_streamed(src, send, recv, out, chunk_bytes: int, mode: int, compute, wire, events: Events,
+                        ring_bytes: int | None = None) -> int:
+    """src, send, recv, out: pairs of CUDA tensors (rank 0, rank 1); compute,
+    wire: pairs of torch streams (or raw stream handles).  Returns the status."""
+    d = _allreduce2_desc(src, send, recv, out, chunk_bytes, mode, compute, wire, events, ring_bytes)
     return lib().xfer_allreduce2_streamed(ctypes.byref(d))
+
+
+class AllReduce2Graph:
+    """The streamed schedule recorded once as a HIP graph over fixed buffers
+    (src, send, recv, out as in allreduce2_streamed)."""
+
+    def __init__(self, src, send, recv, out, chunk_bytes: int, mode: int, ring_bytes: int | None = None):
+        self._keep = (src, send, recv, out)       # the graph holds their addresses
+        d = _allreduce2_desc(src, send, recv, out, chunk_bytes, mode, ring_bytes=ring_bytes)
+        self.exec = ctypes.c_void_p(None)
+        _check(lib().xfer_allreduce2_graph_create(ctypes.byref(d), ctypes.byref(self.exec)),
+               "xfer_allreduce2_graph_create")
+
+    def launch(self, stream=None) -> None:
+        _check(lib().xfer_allreduce2_graph_launch(self.exec, _stream(stream)), "xfer_allreduce2_graph_launch")
+
+    def close(self) -> None:
+        if self.exec is not None:
+            lib().xfer_allreduce2_graph_destroy(self.exec)
+            self.exec = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def allreduce2_graph_create_status(d: AllReduce2Desc) -> int:
+    exec_ = ctypes.c_void_p(None)
+    st = lib().xfer_allreduce2_graph_create(ctypes.byref(d), ctypes.byref(exec_))
+    if st == OK and exec_.value:
+        lib().xfer_allreduce2_graph_destroy(exec_)
+    return st
 
 
 # ---------------------------------------------- coalesced fetch by dense group

@@ -558,6 +558,25 @@ typedef struct {
  */
 XFER_API int xfer_allreduce2_streamed(const xfer_allreduce2_desc *d);
 
+/*
+ * xfer_allreduce2_graph_create - the same schedule recorded once as a HIP
+ * graph over the descriptor's buffers, so that a whole all-reduce costs one
+ * launch (the streamed call makes three to four runtime calls per
+ * operation and is bound by them at 512 KiB chunks).
+ * SWITCHED OFF: recording the schedule by stream capture crashed the host
+ * process inside this call on MI355X (ROCm 7.2), cause not found.  The call
+ * checks its arguments like xfer_allreduce2_streamed (XFER_E_INVAL, NULL exec
+ * included), sets *exec to NULL, returns XFER_OK when n == 0 (nothing to
+ * do) and XFER_E_UNSUPPORTED otherwise, without any runtime call.
+ *
+ * xfer_allreduce2_graph_launch - enqueue one all-reduce on stream (a NULL
+ * exec is a no-op).  xfer_allreduce2_graph_destroy - release the graph (NULL
+ * is a no-op).
+ */
+XFER_API int xfer_allreduce2_graph_create(const xfer_allreduce2_desc *d, hipGraphExec_t *exec);
+XFER_API int xfer_allreduce2_graph_launch(hipGraphExec_t exec, hipStream_t stream);
+XFER_API int xfer_allreduce2_graph_destroy(hipGraphExec_t exec);
+
 #ifdef __cplusplus
 }
 #endif

@@ -114,3 +114,55 @@ def test_prompt_batch_2048x5120_two_512k_slots():
     want = _want(a, b, x.OUT_F32)
     assert np.array_equal(down(outs[0], np.uint32), want)
     assert np.array_equal(down(outs[1], np.uint32), want)
+
+
+GRAPH_OFF = "recording the schedule as a HIP graph crashed the host process inside xfer_allreduce2_graph_create on the GPU box twice; the builder is switched off (it returns XFER_E_UNSUPPORTED) until a cause is found"
+
+
+@pytest.mark.skip(reason=GRAPH_OFF)
+@pytest.mark.parametrize("R", [1, 2, 3])
+@pytest.mark.parametrize("mode", [x.OUT_F32, x.OUT_BF16])
+def test_graph_small_chunks_repeated_launches(R, mode):
+    """The schedule as one HIP graph over fixed buffers: three launches on the
+    current stream, the inputs rewritten on that stream between launches and
+    no host synchronisation until the end; then each launch checked after a
+    synchronisation."""
+    n, chunk = 1001, 64
+    esize = 4 if mode == x.OUT_F32 else 2
+    dt = np.uint32 if mode == x.OUT_F32 else np.uint16
+    a_dev, b_dev = zeros(4 * n), zeros(4 * n)
+    send = [zeros(R * chunk) for _ in range(2)]
+    recv = [zeros(R * chunk) for _ in range(2)]
+    outs = [zeros(n * esize) for _ in range(2)]
+    g = x.AllReduce2Graph((a_dev, b_dev), send, recv, outs, chunk, mode)
+    inputs = [(dg.normal_f32(n, 300 + 7 * k + R, 1.0), dg.normal_f32(n, 400 + 7 * k + R, 1.0)) for k in range(3)]
+    keep = [zeros(n * esize) for _ in range(3)]
+    say("graph streamed R", R, "mode", mode)
+    for k, (a, b) in enumerate(inputs):
+        a_dev.copy_(up(a))
+        b_dev.copy_(up(b))
+        g.launch()
+        keep[k].copy_(outs[k % 2])          # alternate ranks' outputs, ordered on the same stream
+    for k, (a, b) in enumerate(inputs):
+        assert np.array_equal(down(keep[k], dt), _want(a, b, mode)), k
+    assert np.array_equal(down(outs[0], dt), down(outs[1], dt))
+    g.close()
+
+
+@pytest.mark.skip(reason=GRAPH_OFF)
+def test_graph_prompt_batch_2048x5120():
+    n, chunk, R = 2048 * 5120, 512 * 1024, 2
+    a = dg.prompt_partial(n, dg.seed_for(2, 0, 2048))
+    b = dg.prompt_partial(n, dg.seed_for(2, 1, 2048))
+    send = [zeros(R * chunk) for _ in range(2)]
+    recv = [zeros(R * chunk) for _ in range(2)]
+    outs = [zeros(4 * n) for _ in range(2)]
+    da, db = up(a), up(b)
+    g = x.AllReduce2Graph((da, db), send, recv, outs, chunk, x.OUT_F32)
+    say("graph streamed 2048x5120")
+    for _ in range(2):
+        g.launch()
+    want = _want(a, b, x.OUT_F32)
+    assert np.array_equal(down(outs[0], np.uint32), want)
+    assert np.array_equal(down(outs[1], np.uint32), want)
+    g.close()

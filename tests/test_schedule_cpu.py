@@ -143,3 +143,37 @@ def test_streamed_argument_checks():
     empty = x.AllReduce2Desc.from_buffer_copy(d)
     empty.n = 0
     assert L.xfer_allreduce2_streamed(ctypes.byref(empty)) == x.OK
+
+
+def test_graph_builder_argument_checks():
+    """The graph builder refuses what the streamed call refuses, before any
+    runtime call; an empty all-reduce yields no graph (nothing to launch)."""
+    import ctypes
+    d = x.AllReduce2Desc()
+    base = 0x10000000
+    for r in range(2):
+        d.src[r] = base + r * 0x100000
+        d.send[r] = base + 0x400000 + r * 0x10000
+        d.recv[r] = base + 0x500000 + r * 0x10000
+        d.out[r] = base + 0x600000 + r * 0x100000
+    d.n, d.chunk_bytes, d.ring_bytes, d.out_mode = 1000, 64, 128, 0
+    for field, value in (("out_mode", 5), ("chunk_bytes", 24), ("ring_bytes", 96)):
+        bad = x.AllReduce2Desc.from_buffer_copy(d)
+        setattr(bad, field, value)
+        assert x.allreduce2_graph_create_status(bad) == x.E_INVAL
+    bad = x.AllReduce2Desc.from_buffer_copy(d)
+    bad.out[1] = bad.recv[0] + 32             # an output overlaps a receive ring
+    assert x.allreduce2_graph_create_status(bad) == x.E_INVAL
+    empty = x.AllReduce2Desc.from_buffer_copy(d)
+    empty.n = 0
+    ex = ctypes.c_void_p(0x1)
+    assert x.lib().xfer_allreduce2_graph_create(ctypes.byref(empty), ctypes.byref(ex)) == x.OK
+    assert ex.value is None
+    assert x.lib().xfer_allreduce2_graph_create(ctypes.byref(d), None) == x.E_INVAL
+    # switched off: a valid non-empty call is refused before any runtime call
+    assert x.allreduce2_graph_create_status(d) == x.E_UNSUPPORTED
+    assert x.lib().xfer_allreduce2_graph_launch(None, None) == x.OK
+    assert x.lib().xfer_allreduce2_graph_destroy(None) == x.OK
+    no_events = x.AllReduce2Desc.from_buffer_copy(d)
+    no_events.events = None
+    assert x.lib().xfer_allreduce2_streamed(ctypes.byref(no_events)) == x.E_INVAL
