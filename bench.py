@@ -446,7 +446,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}): the hot path here is single-GPU "
-              "by design; see the sharding notes in DESIGN.md", file=sys.stderr)
+              "by design (both ranks are emulated in one HBM)", file=sys.stderr)
         sys.exit(2)
     if args.calib_copy:
         calib_copy()

@@ -116,7 +116,7 @@ def test_prompt_batch_2048x5120_two_512k_slots():
     assert np.array_equal(down(outs[1], np.uint32), want)
 
 
-GRAPH_OFF = "recording the schedule as a HIP graph crashed the host process inside xfer_allreduce2_graph_create on the GPU box twice; the builder is switched off (it returns XFER_E_UNSUPPORTED) until a cause is found"
+GRAPH_OFF = "recording the schedule as a HIP graph crashed the host process inside xfer_allreduce2_graph_create on MI355X (ROCm 7.2), twice; the builder is switched off (it returns XFER_E_UNSUPPORTED) until a cause is found"
 
 
 @pytest.mark.skip(reason=GRAPH_OFF)
