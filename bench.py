@@ -481,12 +481,13 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32+bf16",
+        "dtype": "f32",
         "data": "synthetic",
         "config": {
             "workload": wl["describe"],
             "step_bytes": step_bytes,
             "parallelism": "single GPU; both ranks emulated in one HBM",
+            "wire_dtype": "bf16",
         },
         "kernels": kernels,
         "pack_combine_GBps": (round((ab["pack_rank0"] + ab["pack_rank1"] + ab["combine_f32"]) /
