@@ -317,6 +317,37 @@ def run_gpu(steps, warmup, workload):
     return w, elapsed, per_kernel_ms, roofline_ms
 
 
+def isolated_cold(w, reps=20):
+    """Each kernel of the workload on its own, cold: before every timed
+    repetition a 1 GiB scratch buffer is written with ordinary stores (more
+    than the 256 MB Infinity Cache), then the kernel runs bracketed by HIP
+    events; the median is kept.  In the step, by contrast, a short kernel that
+    follows the gather or scatter shares HBM with their draining writes."""
+    import torch
+
+    scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0")
+    ab = w.algorithmic_bytes()
+    out = {}
+    for name, k in w.kernels():
+        for _ in range(3):
+            k()
+        times = []
+        for r in range(reps):
+            scratch.fill_(r & 0xFF)
+            e0, e1 = _events()
+            e0.record()
+            k()
+            e1.record()
+            e1.synchronize()
+            times.append(e0.elapsed_time(e1))
+        ms = sorted(times)[len(times) // 2]
+        gbs = ab[name] / (ms * 1e-3) / 1e9
+        out[name] = {"us": round(ms * 1e3, 2), "GBps": round(gbs, 1), "frac_of_peak": round(gbs / PEAK_HBM_GBS, 4)}
+    del scratch
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(w, budget_s=12.0):
     """The oracle, as it is, on this host: the same step (same sizes, same
     inputs) repeated until about budget_s seconds of work; buffers are
@@ -443,6 +474,8 @@ def main():
                     help="step (default): the bench line; fragmented: the shuffled-layout / large-combine shapes")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy", action="store_true", help="run only the copy used to scale PMC readings")
+    ap.add_argument("--isolated", action="store_true",
+                    help="also time each kernel alone and cold (1 GiB written between repetitions)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}): the hot path here is single-GPU "
@@ -496,6 +529,9 @@ def main():
         "roofline": roofline,
         "cpu_baseline": None,
     }
+    if args.isolated:
+        log("bench: isolated cold pass")
+        line["isolated_cold"] = isolated_cold(w)
     if not args.no_cpu_baseline and args.workload == "step":
         log("bench: cpu baseline (oracle)")
         line["cpu_baseline"] = cpu_baseline(w)
