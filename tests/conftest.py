@@ -13,8 +13,9 @@ def pytest_configure(config):
 
 
 def _ensure_cpu_libs():
-    """The oracle and the input generators are plain gcc builds; build them
-    only when nothing is built yet (after a source change, rebuild with
+    """The oracle and the input generators are plain gcc builds, and the HIP
+    library cross-compiles with hipcc without a GPU; each is built only when
+    nothing is built yet (after a source change, rebuild with
     __graft_entry__.build())."""
     from oracle import build as ob
     from datagen import build as db
@@ -22,6 +23,9 @@ def _ensure_cpu_libs():
         ob.build()
     if not os.path.exists(db.LIB):
         db.build()
+    from bf16_wire_all_amd import build as xb
+    if not os.path.exists(xb.LIB):
+        xb.build()
 
 
 _ensure_cpu_libs()
