@@ -318,32 +318,44 @@ def run_gpu(steps, warmup, workload):
 
 
 def isolated_cold(w, reps=20):
-    """Each kernel of the workload on its own, cold: before every timed
-    repetition a 1 GiB scratch buffer is written with ordinary stores (more
-    than the 256 MB Infinity Cache), then the kernel runs bracketed by HIP
-    events; the median is kept.  In the step, by contrast, a short kernel that
-    follows the gather or scatter shares HBM with their draining writes."""
+    """Each kernel of the workload on its own, cold, two ways, each kept as
+    the median of `reps` event-timed repetitions:
+      after_write:      before every repetition a 1 GiB scratch buffer is
+                        written with ordinary stores (more than the 256 MB
+                        Infinity Cache); the cache is then full of dirty
+                        lines whose write-back shares HBM with the kernel;
+      after_write_read: the same write, then a second 1 GiB buffer is read
+                        (summed), which evicts those dirty lines first, so
+                        the kernel starts on a cache full of clean,
+                        unrelated data.
+    In the step, by contrast, a short kernel that follows the gather or
+    scatter shares HBM with their draining writes."""
     import torch
 
     scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0")
+    other = torch.ones(1 << 30, dtype=torch.uint8, device="cuda:0")
     ab = w.algorithmic_bytes()
-    out = {}
-    for name, k in w.kernels():
-        for _ in range(3):
-            k()
-        times = []
-        for r in range(reps):
-            scratch.fill_(r & 0xFF)
-            e0, e1 = _events()
-            e0.record()
-            k()
-            e1.record()
-            e1.synchronize()
-            times.append(e0.elapsed_time(e1))
-        ms = sorted(times)[len(times) // 2]
-        gbs = ab[name] / (ms * 1e-3) / 1e9
-        out[name] = {"us": round(ms * 1e3, 2), "GBps": round(gbs, 1), "frac_of_peak": round(gbs / PEAK_HBM_GBS, 4)}
-    del scratch
+    out = {"after_write": {}, "after_write_read": {}}
+    for mode in out:
+        for name, k in w.kernels():
+            for _ in range(3):
+                k()
+            times = []
+            for r in range(reps):
+                scratch.fill_(r & 0xFF)
+                if mode == "after_write_read":
+                    other.sum()
+                e0, e1 = _events()
+                e0.record()
+                k()
+                e1.record()
+                e1.synchronize()
+                times.append(e0.elapsed_time(e1))
+            ms = sorted(times)[len(times) // 2]
+            gbs = ab[name] / (ms * 1e-3) / 1e9
+            out[mode][name] = {"us": round(ms * 1e3, 2), "GBps": round(gbs, 1),
+                               "frac_of_peak": round(gbs / PEAK_HBM_GBS, 4)}
+    del scratch, other
     torch.cuda.empty_cache()
     return out
 
