@@ -166,7 +166,7 @@ class Workload:
             pos_ = pos if pos is not None else np.arange(B, dtype=np.uint32)
             bb = np.repeat(np.arange(B, dtype=np.int64), 2 * S)
             jj = np.tile(np.arange(2 * S, dtype=np.int64), B)
-            self.page_plans, self.page_bufs = [], []
+            self.page_plans, self.page_bufs, self.page_idx = [], [], []
             for r in range(2):
                 si = (pos_.astype(np.int64)[bb] * 2 * S + jj).astype(np.uint32)
                 di = (bb * L + r * 2 * S + jj).astype(np.uint32)
@@ -175,6 +175,7 @@ class Workload:
                                                        (self.staging.data_ptr(), self.staging.numel()), di, SG, 0,
                                                        buf))
                 self.page_bufs.append(buf)
+                self.page_idx.append((si, di))
             k = np.arange(B * L, dtype=np.int64)
             di = (((k // L) * N_SLOTS + (k % L) // 2) * 3 + (k % L) % 2).astype(np.uint32)
             buf = torch.zeros(x.pages_plan_bytes(k.size), dtype=torch.uint8, device=dev)
@@ -182,6 +183,7 @@ class Workload:
                                                 k.astype(np.uint32), SG, 0, (self.dst.data_ptr(), self.dst.numel()),
                                                 di, SG, 0, buf)
             self.page_bufs.append(buf)
+            self.page_idx.append((k.astype(np.uint32), di))
         self.f32wire = f32wire
         if f32wire:
             # BF16 results of the F32-wire sum: the drafter's 20 rows, and the whole partials

@@ -1,13 +1,15 @@
 // Execution of a descriptor list: every descriptor is one contiguous copy of
 // `bytes` from a device address into the slab.  A descriptor is cut into
-// 4 KiB units and its two halves are walked side by side: workgroup piece c
-// copies unit c and unit c + ceil(units / 2), each thread one 16-byte vector
-// of each, every load followed by its store (nontemporal both ways).  On
-// MI355X this two-stream shape measured 6.4-6.7 TB/s for a plain 2.36 GB copy
-// against 5.9 TB/s for one contiguous 8 KiB piece per workgroup with both
-// loads issued first.  The grid is n_descs x max_pieces (max_pieces = the
-// largest descriptor's ceil(bytes / 8 KiB)); workgroups past a shorter
-// descriptor's half exit at once.
+// 4 KiB units, grouped into tiles of 2T units (T = min(576, ceil(units / 2)));
+// workgroup piece c of a tile copies unit c and unit c + T, each thread one
+// 16-byte vector of each, every load followed by its store (nontemporal both
+// ways).  On MI355X the two-stream shape measured 6.4-6.7 TB/s for a plain
+// 2.36 GB copy, fastest with the streams about 1.2 MB apart, against 5.9 TB/s
+// for one contiguous 8 KiB piece per workgroup with both loads issued first;
+// on the 72-read fetch, tiles of 2 x 576 units beat pairing the two halves of
+// each 32 MiB read by 4 % (6.52 against 6.27 TB/s; 2 x 288 units: 6.47).  The grid is
+// n_descs x max_pieces (max_pieces from the largest descriptor); workgroups
+// past a shorter descriptor's end exit at once.
 #include "internal.h"
 
 namespace xfer {
@@ -33,10 +35,12 @@ __global__ __launch_bounds__(kThreads) void copy_descs_kernel(const xfer_desc *d
   const uint32_t piece = blockIdx.x - d * max_pieces;
   const xfer_desc desc = descs[d];
   const uint64_t n_units = (desc.bytes + kUnitBytes - 1) / kUnitBytes;
-  const uint64_t half = (n_units + 1) / 2;  // == ceil(bytes / 8 KiB)
-  if (piece >= half) return;
-  copy_unit(desc, slab, piece);
-  if (piece + half < n_units) copy_unit(desc, slab, piece + half);
+  const uint64_t T = pair_span(n_units);  // >= 1: bytes > 0 (host check)
+  const uint64_t t = piece / T, c = piece - t * T;
+  const uint64_t u0 = t * 2 * T + c;
+  if (u0 >= n_units) return;
+  copy_unit(desc, slab, u0);
+  if (u0 + T < n_units) copy_unit(desc, slab, u0 + T);
 }
 
 static_assert(kUnitBytes == 16 * kThreads, "one vector per thread per unit");

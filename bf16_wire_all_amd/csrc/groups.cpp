@@ -150,7 +150,7 @@ int xfer_descs_prepare(const xfer_desc *descs, uint64_t n_descs, uint64_t slab_b
   if (!out || (n_descs && !descs) || n_regions < 0 || (n_regions > 0 && !regions)) return XFER_E_INVAL;
   for (int i = 0; i < n_regions; ++i)
     if (regions[i].base > UINT64_MAX - regions[i].bytes) return XFER_E_INVAL;
-  uint64_t lo_all = UINT64_MAX, hi_all = 0, max_bytes = 0;
+  uint64_t lo_all = UINT64_MAX, hi_all = 0;
   std::vector<std::pair<uint64_t, uint64_t>> dst(n_descs);
   for (uint64_t i = 0; i < n_descs; ++i) {
     const xfer_desc &d = descs[i];
@@ -164,12 +164,13 @@ int xfer_descs_prepare(const xfer_desc *descs, uint64_t n_descs, uint64_t slab_b
     dst[i] = {d.dst_off, d.bytes};
     lo_all = std::min(lo_all, d.src);
     hi_all = std::max(hi_all, d.src + d.bytes);
-    max_bytes = std::max(max_bytes, d.bytes);
   }
   std::sort(dst.begin(), dst.end());
   for (size_t i = 1; i < dst.size(); ++i)
     if (dst[i].first < dst[i - 1].first + dst[i - 1].second) return XFER_E_OVERLAP;
-  const uint64_t pieces = (max_bytes + xfer::kDescPieceBytes - 1) / xfer::kDescPieceBytes;
+  uint64_t pieces = 0;  // workgroups per descriptor slot of the grid: the largest descriptor's
+  for (uint64_t i = 0; i < n_descs; ++i)
+    pieces = std::max(pieces, xfer::paired_pieces((descs[i].bytes + 4095) / 4096));
   if (pieces > UINT32_MAX || (n_descs && pieces * n_descs > xfer::kMaxGridBlocks)) return XFER_E_UNSUPPORTED;
   const uint64_t need = xfer_descs_plan_bytes(n_descs);
   if (need && (!dev || ((uintptr_t)dev & 15u) || dev_bytes < need)) return XFER_E_INVAL;

@@ -34,6 +34,8 @@ struct PagesView {
   const uint32_t *src_idx, *dst_idx;
   uint64_t src_base, src_stride, dst_base, dst_stride, page_len;
   uint32_t units_per_page, n_units;
+  uint32_t span;    // a workgroup copies units c and c + span of a tile of 2 * span units
+  uint32_t pieces;  // workgroups: ceil(n_units / (2 * span)) * span
 };
 hipError_t launch_paged_copy(const PagesView &v, hipStream_t stream);
 
@@ -87,8 +89,21 @@ constexpr uint32_t kMaxSegVectors = 1u << 16;  // 1 MiB segments
 hipError_t launch_gather(const PlanView &p, void *staging, hipStream_t stream);
 hipError_t launch_scatter(const PlanView &p, const void *staging, hipStream_t stream);
 
-// ---- descriptor copies (descs_copy.hip)
-constexpr uint32_t kDescPieceBytes = 8192;
+// ---- descriptor copies (descs_copy.hip) and paged copies (pages_copy.hip)
+// Both cut their work into 4 KiB units and give a workgroup two units of a
+// tile of 2T units, T apart: unit c and unit c + T of the tile, with
+// T = min(kPairSpan, ceil(units / 2)).
+constexpr uint32_t kDescPieceBytes = 8192;  // two units: the work of one workgroup
+constexpr uint64_t kPairSpan = 576;         // units between a workgroup's two units (2.25 MiB)
+__host__ __device__ inline uint64_t pair_span(uint64_t units) {
+  const uint64_t half = (units + 1) / 2;
+  return half < kPairSpan ? half : kPairSpan;
+}
+// Workgroups for a list of `units` units: ceil(units / 2T) tiles of T.
+__host__ __device__ inline uint64_t paired_pieces(uint64_t units) {
+  const uint64_t T = pair_span(units);
+  return T ? (units + 2 * T - 1) / (2 * T) * T : 0;
+}
 hipError_t launch_copy_descs(const xfer_desc *descs, uint64_t n_descs, uint32_t max_pieces, void *slab,
                              hipStream_t stream);
 

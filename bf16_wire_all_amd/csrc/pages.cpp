@@ -42,7 +42,7 @@ int xfer_pages_prepare(uint64_t page_len, const xfer_region *src, const xfer_pag
   const uint64_t upp = (page_len + xfer::kPageUnitBytes - 1) / xfer::kPageUnitBytes;
   if (upp > UINT32_MAX || (n_pages && n_pages > UINT32_MAX / upp)) return XFER_E_UNSUPPORTED;
   const uint64_t n_units = n_pages * upp;
-  if ((n_units + 1) / 2 > xfer::kMaxGridBlocks) return XFER_E_UNSUPPORTED;
+  if (xfer::paired_pieces(n_units) > xfer::kMaxGridBlocks) return XFER_E_UNSUPPORTED;
   std::vector<uint64_t> starts(n_pages);
   for (uint64_t k = 0; k < n_pages; ++k) {
     uint64_t s, d;
@@ -96,6 +96,8 @@ int xfer_paged_copy(const xfer_pages_plan *plan, hipStream_t stream) {
   v.page_len = plan->page_len;
   v.units_per_page = plan->units_per_page;
   v.n_units = (uint32_t)(plan->n_pages * plan->units_per_page);
+  v.span = (uint32_t)xfer::pair_span(v.n_units);
+  v.pieces = (uint32_t)xfer::paired_pieces(v.n_units);
   if (xfer::launch_paged_copy(v, stream) != hipSuccess) return XFER_E_DEVICE;
   return XFER_OK;
 }

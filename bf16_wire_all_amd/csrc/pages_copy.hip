@@ -1,10 +1,14 @@
 // Paged copy by two Pages lists (indices, stride, offset): source page k to
 // destination page k.  Pages are cut into 4 KiB units (the last unit of a
-// page may be shorter); workgroup c copies unit c and unit c + gridDim.x,
-// one 16-byte vector per thread each, every nontemporal load followed by its
-// store: the two-stream shape that measured fastest for plain copies on
-// MI355X.  Unit u is page u / units_per_page, bytes from 4096 * (u mod
-// units_per_page); the two page indices are uniform loads.
+// page may be shorter).  The units form tiles of 2 * span units, span =
+// min(576, ceil(units / 2)); workgroup c of a tile copies its unit c and unit
+// c + span, one 16-byte vector per thread each, every nontemporal load
+// followed by its store: the two-stream shape that measured fastest for plain
+// copies on MI355X.  On the 288,000-page gathers of 4 KiB pages, span 576 ran
+// at 6.30 TB/s against 6.11 for the two halves of the list (the scatter of
+// 576,000 pages: 6.14 against 6.12).  Unit u is page u / units_per_page,
+// bytes from 4096 * (u mod units_per_page); the two page indices are uniform
+// loads.
 #include "internal.h"
 
 namespace xfer {
@@ -28,15 +32,17 @@ __device__ __forceinline__ void copy_unit(const PagesView &v, uint32_t u) {
 }
 
 __global__ __launch_bounds__(kThreads) void paged_copy_kernel(PagesView v) {
-  copy_unit(v, blockIdx.x);  // blockIdx.x < ceil(n_units / 2) <= n_units
-  const uint32_t u1 = blockIdx.x + gridDim.x;
-  if (u1 < v.n_units) copy_unit(v, u1);
+  const uint32_t t = blockIdx.x / v.span, c = blockIdx.x - t * v.span;
+  const uint64_t u0 = (uint64_t)t * 2 * v.span + c;
+  if (u0 >= v.n_units) return;
+  copy_unit(v, (uint32_t)u0);
+  if (u0 + v.span < v.n_units) copy_unit(v, (uint32_t)(u0 + v.span));
 }
 
 }  // namespace
 
 hipError_t launch_paged_copy(const PagesView &v, hipStream_t stream) {
-  const dim3 grid((uint32_t)(((uint64_t)v.n_units + 1) / 2));
+  const dim3 grid(v.pieces);
   return launch(paged_copy_kernel, grid, dim3(kThreads), 0, stream, v);
 }
 

@@ -398,8 +398,8 @@ XFER_API size_t xfer_descs_plan_bytes(uint64_t n_descs);
  * no source range wraps or leaves the declared regions (XFER_E_RANGE), the
  * destination ranges lie in [0, slab_bytes) and are pairwise disjoint
  * (XFER_E_OVERLAP).  dev: device, 16-byte aligned, xfer_descs_plan_bytes().
- * XFER_E_UNSUPPORTED if n_descs times the largest descriptor's 8 KiB pieces
- * exceeds 2^24 - 1 (the kernel's grid).
+ * XFER_E_UNSUPPORTED if n_descs times the largest descriptor's workgroup
+ * count (about one per 8 KiB) exceeds 2^24 - 1 (the kernel's grid).
  */
 XFER_API int xfer_descs_prepare(const xfer_desc *descs, uint64_t n_descs, uint64_t slab_bytes,
                                 const xfer_region *regions, int n_regions, void *dev, size_t dev_bytes,

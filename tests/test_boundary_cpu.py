@@ -266,10 +266,12 @@ def test_launch_size_limits():
     t = _table([1], [big], [4096], [1 << 25], 1 << 25, seg=4096)
     st, _ = x.runs_prepare_status(t, [(big, 1 << 37)], False, 0x1000, 1 << 30)
     assert st == x.E_UNSUPPORTED
-    # descriptors: one read of 2^24 pieces of 8 KiB
-    d = np.array([(big, 0, 1 << 37)], x.DESC)
-    st, _ = x.descs_prepare_status(d, 1 << 37, [(big, 1 << 38)], 0x1000, 1 << 20)
+    # descriptors: 4 KiB units paired in tiles of 2 x 288, one workgroup per pair: the largest read that
+    # fits 2^24 - 1 workgroups is 58,254 tiles of 576 units
+    top = 58254 * 576 * 4096
+    d = np.array([(big, 0, top + 4096)], x.DESC)                         # one unit more: a 58,255th tile
+    st, _ = x.descs_prepare_status(d, 1 << 38, [(big, 1 << 38)], 0x1000, 1 << 20)
     assert st == x.E_UNSUPPORTED
-    d = np.array([(big, 0, (1 << 37) - 8192)], x.DESC)                  # one piece fewer: accepted
-    st, _ = x.descs_prepare_status(d, 1 << 37, [(big, 1 << 38)], 0, 0)
-    assert st == x.E_INVAL                                              # ...up to the missing device buffer
+    d = np.array([(big, 0, top)], x.DESC)
+    st, _ = x.descs_prepare_status(d, 1 << 38, [(big, 1 << 38)], 0, 0)
+    assert st == x.E_INVAL                                              # accepted up to the missing device buffer

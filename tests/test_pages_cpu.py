@@ -156,6 +156,20 @@ def test_library_refuses_oversized_launches():
                  dst=(1 << 46, 1 << 45)) == x.E_UNSUPPORTED             # more than 2^32 - 1 units
 
 
+def test_launch_limit_boundary():
+    """Workgroups pair units 576 apart in tiles of 1152 units, 576 workgroups a
+    tile: 29127 tiles (33,554,304 units) fit under 2^24 - 1 workgroups, one
+    unit more needs a 29128th tile and is refused."""
+    n = 262143                                                            # 512 KiB pages: 128 units each
+    idx = np.arange(n, dtype=np.uint32)
+    assert _prep(page_len=1 << 19, si=idx, ss=1 << 19, di=idx, ds=1 << 19, src=(1 << 40, 1 << 38),
+                 dst=(1 << 41, 1 << 38)) == x.E_INVAL                    # accepted; then no device buffer
+    n = 33554305 // 5                                                     # 16400-byte pages: 5 units each
+    idx = np.arange(n, dtype=np.uint32)
+    assert _prep(page_len=16400, si=idx, ss=16400, di=idx, ds=16400, src=(1 << 40, 1 << 38),
+                 dst=(1 << 41, 1 << 38)) == x.E_UNSUPPORTED
+
+
 def test_library_agrees_with_oracle_on_what_is_refused():
     """The same lists, refused or accepted alike by the oracle and the library."""
     cases = [dict(si=(0, 256)), dict(di=(255, 256)), dict(di=(0, 1), ds=2048), dict(si=(0, 1))]
