@@ -188,15 +188,21 @@ __global__ __launch_bounds__(64) void argmax_fold_kernel(Shards sh, uint32_t spl
   const Rec &lose1 = x_wins ? y1 : x1;
   const Rec &win2 = x_wins ? x2 : y2;
   const Rec &top2 = before(lose1, win2) ? lose1 : win2;
-  // Exact bits of the chosen elements (the key does not keep the sign of 0).
-  const uint32_t v1 = sh.ptr[top1.shard][(uint64_t)row * sh.ld[top1.shard] + top1.col];
+  // Exact bits of a chosen element: ord16 is one-to-one except that -0 and +0
+  // share 0x8000, so only a zero is read back from the row for its sign.
+  auto bits_of = [&](const Rec &r) -> uint32_t {
+    if (r.ord > 0x8000u) return r.ord - 0x8000u;
+    if (r.ord < 0x8000u) return 0x8000u | (0x8000u - r.ord);
+    return sh.ptr[r.shard][(uint64_t)row * sh.ld[r.shard] + r.col];
+  };
+  const uint32_t v1 = bits_of(top1);
   if (MODE == XFER_ARGMAX) {
     xfer_max_idx r;
     r.max = __uint_as_float(v1 << 16);
     r.idx = (int32_t)top1.gid;
     reinterpret_cast<xfer_max_idx *>(out)[row] = r;
   } else {
-    const uint32_t v2 = sh.ptr[top2.shard][(uint64_t)row * sh.ld[top2.shard] + top2.col];
+    const uint32_t v2 = bits_of(top2);
     xfer_top2 r;
     r.top1 = __uint_as_float(v1 << 16);
     r.top2 = __uint_as_float(v2 << 16);

@@ -129,3 +129,23 @@ def test_failed_call_leaves_output_untouched():
     ws = zeros(4096)
     assert x.argmax_merge_raw(s0, s1, x.TOP2, out.data_ptr(), ws.data_ptr(), 4096) == x.E_INVAL
     assert np.all(down(out) == 7)
+
+
+def test_every_value_wins_with_its_own_bits():
+    """Every BF16 pattern but NaN is once a row's top1 (the rest of the row
+    -inf) and once a row's top2 (under a planted +inf): both records carry the
+    chosen element's exact bits, the sign of a zero included."""
+    p = np.arange(1 << 16, dtype=np.uint32)
+    pats = p[(p & 0x7FFF) <= 0x7F80].astype(np.uint16)
+    n, cols, split = pats.size, 80, 40
+    i = np.arange(n)
+    m = np.full((2 * n, cols), 0xFF80, np.uint16)
+    m[i, (i * 13) % cols] = pats                               # rows [0, n): pats[i] is top1
+    c = (i * 29 + 5) % cols
+    m[n + i, c] = pats                                         # rows [n, 2n): pats[i] is top2 ...
+    m[n + i, (c + 1 + i % (cols - 1)) % cols] = 0x7F80          # ... under a +inf elsewhere in the row
+    say(f"argmax: every value as winner, {2 * n} rows x {cols}")
+    want = _check_matrix(m, split, calls=1)
+    rec_v = want.view(x.TOP2_REC)
+    assert np.array_equal(np.asarray(rec_v["top1"][:n]).view(np.uint32) >> 16, pats)
+    assert np.array_equal(np.asarray(rec_v["top2"][n:]).view(np.uint32) >> 16, pats)
