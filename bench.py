@@ -331,15 +331,42 @@ def isolated_cold(w, reps=20):
                         the kernel starts on a cache full of clean,
                         unrelated data.
     In the step, by contrast, a short kernel that follows the gather or
-    scatter shares HBM with their draining writes."""
+    scatter shares HBM with their draining writes.
+
+    Beside every kernel that moves at least 1 MB, the same cold protocol
+    times two plain copies of the same algorithmic bytes (half read, half
+    written): the HIP runtime's device-to-device copy, and the library's own
+    128-bit copy (xfer_copy_descs over 32 MiB descriptors, the coalesced
+    fetch's kernel).  They are the on-box ceiling at that size."""
+    import numpy as np
     import torch
+
+    import bf16_wire_all_amd as x
 
     scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0")
     other = torch.ones(1 << 30, dtype=torch.uint8, device="cuda:0")
     ab = w.algorithmic_bytes()
+    calls = list(w.kernels())
+    for name, _ in list(calls):
+        half = ab[name] // 2 // 16 * 16
+        if half < (1 << 19):
+            continue
+        src = torch.full((half,), 0x5A, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty(half, dtype=torch.uint8, device="cuda:0")
+        n_d = -(-half // x.MAX_READ_BYTES)
+        descs = np.zeros(n_d, x.DESC)
+        descs["src"] = src.data_ptr() + np.arange(n_d, dtype=np.uint64) * x.MAX_READ_BYTES
+        descs["dst_off"] = np.arange(n_d, dtype=np.uint64) * x.MAX_READ_BYTES
+        descs["bytes"] = np.minimum(x.MAX_READ_BYTES, half - np.arange(n_d, dtype=np.int64) * x.MAX_READ_BYTES)
+        buf = torch.zeros(x.descs_plan_bytes(n_d), dtype=torch.uint8, device="cuda:0")
+        plan = x.descs_prepare(descs, half, [(src.data_ptr(), half)], buf)
+        calls.append((f"ceiling_runtime_copy@{name}", lambda s=src, d=dst: d.copy_(s)))
+        calls.append((f"ceiling_lib_copy@{name}", lambda p=plan, d=dst: x.copy_descs(p, d)))
+        ab[f"ceiling_runtime_copy@{name}"] = ab[f"ceiling_lib_copy@{name}"] = 2 * half
+        w._ceiling_keep = getattr(w, "_ceiling_keep", []) + [src, dst, buf]
     out = {"after_write": {}, "after_write_read": {}}
     for mode in out:
-        for name, k in w.kernels():
+        for name, k in calls:
             for _ in range(3):
                 k()
             times = []
@@ -358,6 +385,7 @@ def isolated_cold(w, reps=20):
             out[mode][name] = {"us": round(ms * 1e3, 2), "GBps": round(gbs, 1),
                                "frac_of_peak": round(gbs / PEAK_HBM_GBS, 4)}
     del scratch, other
+    w._ceiling_keep = []
     torch.cuda.empty_cache()
     return out
 
