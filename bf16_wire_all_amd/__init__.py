@@ -19,7 +19,7 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libxfer.so")
 
-OK, E_INVAL, E_UNSUPPORTED, E_TABLE, E_RANGE, E_OVERLAP, E_DEVICE = range(7)
+OK, E_INVAL, E_UNSUPPORTED, E_TABLE, E_RANGE, E_OVERLAP, E_DEVICE, E_HOST_MEMORY = range(8)
 OUT_F32, OUT_BF16 = 0, 1
 ARGMAX, TOP2 = 0, 1
 

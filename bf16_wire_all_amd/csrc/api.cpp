@@ -225,6 +225,7 @@ const char *xfer_status_str(int status) {
     case XFER_E_RANGE: return "segment outside the declared regions or address overflow";
     case XFER_E_OVERLAP: return "destination segments overlap";
     case XFER_E_DEVICE: return "HIP runtime error";
+    case XFER_E_HOST_MEMORY: return "host memory for set-up scratch could not be allocated";
     default: return "unknown status";
   }
 }
@@ -389,7 +390,9 @@ int xfer_runs_encode(const uint64_t *addrs, uint32_t n_lanes, uint32_t n_blocks,
 }
 
 int xfer_runs_validate(const xfer_run_table *t, const xfer_region *regions, int n_regions, int is_dst) {
-  return validate_table(t, regions, n_regions, is_dst, nullptr, nullptr);
+  return xfer::guarded([&]() -> int {
+    return validate_table(t, regions, n_regions, is_dst, nullptr, nullptr);
+  });
 }
 
 size_t xfer_runs_plan_bytes(const xfer_run_table *t) {
@@ -399,64 +402,66 @@ size_t xfer_runs_plan_bytes(const xfer_run_table *t) {
 
 int xfer_runs_prepare(const xfer_run_table *t, const xfer_region *regions, int n_regions, int is_dst, void *dev,
                       size_t dev_bytes, xfer_runs_plan *out) {
-  uint64_t span_lo = 0, span_hi = 0;
-  const int st = validate_table(t, regions, n_regions, is_dst, &span_lo, &span_hi);
-  if (st != XFER_OK) return st;
-  if (!out) return XFER_E_INVAL;
-  const Layout L = layout_for(t);
-  if ((uint64_t)L.lane_slots * L.n_tiles * L.pieces > xfer::kMaxGridBlocks) return XFER_E_UNSUPPORTED;
-  if (L.total && (!dev || !aligned16(dev) || dev_bytes < L.total)) return XFER_E_INVAL;
+  return xfer::guarded([&]() -> int {
+    uint64_t span_lo = 0, span_hi = 0;
+    const int st = validate_table(t, regions, n_regions, is_dst, &span_lo, &span_hi);
+    if (st != XFER_OK) return st;
+    if (!out) return XFER_E_INVAL;
+    const Layout L = layout_for(t);
+    if ((uint64_t)L.lane_slots * L.n_tiles * L.pieces > xfer::kMaxGridBlocks) return XFER_E_UNSUPPORTED;
+    if (L.total && (!dev || !aligned16(dev) || dev_bytes < L.total)) return XFER_E_INVAL;
 
-  // Host image of the plan: per (lane, group of blocks) the run covering the
-  // group's first block, then each lane's end; per run its first block
-  // within its lane.
-  std::vector<uint8_t> img(L.total, 0);
-  uint32_t *group_run = reinterpret_cast<uint32_t *>(img.data() + L.off_group_run);
-  uint32_t *run_start = reinterpret_cast<uint32_t *>(img.data() + L.off_run_start);
-  uint64_t r = 0;
-  for (uint32_t l = 0; l < t->n_lanes; ++l) {
-    uint32_t *gr = group_run + (uint64_t)l * (L.n_groups + 1);
-    uint32_t start = 0, group = 0;
-    for (uint32_t k = 0; k < t->runs_per_lane[l]; ++k, ++r) {
-      run_start[r] = start;
-      const uint32_t end = start + t->run_count[r];
-      // every group whose first block lies in [start, end) starts in run r
-      while (group < L.n_groups && (uint64_t)group * L.group_blocks < end) gr[group++] = (uint32_t)r;
-      start = end;
+    // Host image of the plan: per (lane, group of blocks) the run covering the
+    // group's first block, then each lane's end; per run its first block
+    // within its lane.
+    std::vector<uint8_t> img(L.total, 0);
+    uint32_t *group_run = reinterpret_cast<uint32_t *>(img.data() + L.off_group_run);
+    uint32_t *run_start = reinterpret_cast<uint32_t *>(img.data() + L.off_run_start);
+    uint64_t r = 0;
+    for (uint32_t l = 0; l < t->n_lanes; ++l) {
+      uint32_t *gr = group_run + (uint64_t)l * (L.n_groups + 1);
+      uint32_t start = 0, group = 0;
+      for (uint32_t k = 0; k < t->runs_per_lane[l]; ++k, ++r) {
+        run_start[r] = start;
+        const uint32_t end = start + t->run_count[r];
+        // every group whose first block lies in [start, end) starts in run r
+        while (group < L.n_groups && (uint64_t)group * L.group_blocks < end) gr[group++] = (uint32_t)r;
+        start = end;
+      }
+      gr[L.n_groups] = (uint32_t)r;
     }
-    gr[L.n_groups] = (uint32_t)r;
-  }
-  if (t->n_runs) {
-    std::memcpy(img.data() + L.off_run_base, t->run_base, t->n_runs * 8);
-    int64_t *strides = reinterpret_cast<int64_t *>(img.data() + L.off_run_stride);
-    for (uint64_t i = 0; i < t->n_runs; ++i) strides[i] = t->run_count[i] > 1 ? t->run_stride[i] : 0;
-  }
-  if (L.total && hipMemcpy(dev, img.data(), L.total, hipMemcpyHostToDevice) != hipSuccess) return XFER_E_DEVICE;
+    if (t->n_runs) {
+      std::memcpy(img.data() + L.off_run_base, t->run_base, t->n_runs * 8);
+      int64_t *strides = reinterpret_cast<int64_t *>(img.data() + L.off_run_stride);
+      for (uint64_t i = 0; i < t->n_runs; ++i) strides[i] = t->run_count[i] > 1 ? t->run_stride[i] : 0;
+    }
+    if (L.total && hipMemcpy(dev, img.data(), L.total, hipMemcpyHostToDevice) != hipSuccess) return XFER_E_DEVICE;
 
-  xfer_runs_plan p;
-  std::memset(&p, 0, sizeof(p));
-  p.dev = dev;
-  p.dev_bytes = dev_bytes;
-  p.n_lanes = t->n_lanes;
-  p.n_blocks = t->n_blocks;
-  p.seg_bytes = t->seg_bytes;
-  p.n_runs = t->n_runs;
-  p.span_lo = span_lo;
-  p.span_hi = span_hi;
-  p.is_dst = is_dst ? 1u : 0u;
-  p.tile_blocks = L.tile_blocks;
-  p.n_tiles = L.n_tiles;
-  p.group_blocks = L.group_blocks;
-  p.n_groups = L.n_groups;
-  p.pieces = L.pieces;
-  p.lanes_per_wg = L.lanes_per_wg;
-  p.magic = kPlanMagic;
-  p.off_group_run = L.off_group_run;
-  p.off_run_start = L.off_run_start;
-  p.off_run_base = L.off_run_base;
-  p.off_run_stride = L.off_run_stride;
-  *out = p;
-  return XFER_OK;
+    xfer_runs_plan p;
+    std::memset(&p, 0, sizeof(p));
+    p.dev = dev;
+    p.dev_bytes = dev_bytes;
+    p.n_lanes = t->n_lanes;
+    p.n_blocks = t->n_blocks;
+    p.seg_bytes = t->seg_bytes;
+    p.n_runs = t->n_runs;
+    p.span_lo = span_lo;
+    p.span_hi = span_hi;
+    p.is_dst = is_dst ? 1u : 0u;
+    p.tile_blocks = L.tile_blocks;
+    p.n_tiles = L.n_tiles;
+    p.group_blocks = L.group_blocks;
+    p.n_groups = L.n_groups;
+    p.pieces = L.pieces;
+    p.lanes_per_wg = L.lanes_per_wg;
+    p.magic = kPlanMagic;
+    p.off_group_run = L.off_group_run;
+    p.off_run_start = L.off_run_start;
+    p.off_run_base = L.off_run_base;
+    p.off_run_stride = L.off_run_stride;
+    *out = p;
+    return XFER_OK;
+  });
 }
 
 int xfer_gather_runs(const xfer_runs_plan *plan, void *staging, size_t staging_bytes, hipStream_t stream) {

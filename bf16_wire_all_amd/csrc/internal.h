@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <new>
+#include <stdexcept>
 #include <type_traits>
 
 #include "xfer.h"
@@ -20,6 +22,21 @@ static inline hipError_t launch(void (*kernel)(KArgs...), dim3 grid, dim3 block,
   static_assert((std::is_same<KArgs, Args>::value && ...), "argument types must match the kernel exactly");
   void *argv[] = {(void *)&args...};
   return hipLaunchKernel((const void *)kernel, grid, block, argv, lds, stream);
+}
+
+// Runs a set-up call's body and turns a failed host allocation into a status,
+// so that no C++ exception crosses the C interface.
+template <typename F>
+inline int guarded(F &&body) noexcept {
+  try {
+    return body();
+  } catch (const std::bad_alloc &) {
+    return XFER_E_HOST_MEMORY;
+  } catch (const std::length_error &) {
+    return XFER_E_HOST_MEMORY;
+  } catch (...) {
+    return XFER_E_INVAL;
+  }
 }
 
 // A dispatch holds at most 2^32 - 1 work-items along x (the packet's grid

@@ -31,54 +31,56 @@ size_t xfer_pages_plan_bytes(uint64_t n_pages) { return (size_t)(2 * up16(n_page
 
 int xfer_pages_prepare(uint64_t page_len, const xfer_region *src, const xfer_pages *sp, const xfer_region *dst,
                        const xfer_pages *dp, uint64_t n_pages, void *dev, size_t dev_bytes, xfer_pages_plan *out) {
-  if (!out || !src || !dst || !sp || !dp) return XFER_E_INVAL;
-  if (n_pages && (!sp->indices || !dp->indices)) return XFER_E_INVAL;
-  if (page_len == 0 || !aligned16(page_len)) return XFER_E_INVAL;
-  if (!aligned16(sp->stride) || !aligned16(sp->offset) || !aligned16(dp->stride) || !aligned16(dp->offset))
-    return XFER_E_INVAL;
-  if (!aligned16(src->base) || !aligned16(dst->base)) return XFER_E_INVAL;
-  if (src->base > UINT64_MAX - src->bytes || dst->base > UINT64_MAX - dst->bytes) return XFER_E_INVAL;
-  if (src->base < dst->base + dst->bytes && dst->base < src->base + src->bytes) return XFER_E_INVAL;
-  const uint64_t upp = (page_len + xfer::kPageUnitBytes - 1) / xfer::kPageUnitBytes;
-  if (upp > UINT32_MAX || (n_pages && n_pages > UINT32_MAX / upp)) return XFER_E_UNSUPPORTED;
-  const uint64_t n_units = n_pages * upp;
-  if (xfer::paired_pieces(n_units) > xfer::kMaxGridBlocks) return XFER_E_UNSUPPORTED;
-  std::vector<uint64_t> starts(n_pages);
-  for (uint64_t k = 0; k < n_pages; ++k) {
-    uint64_t s, d;
-    if (!page_at(sp->indices[k], *sp, page_len, src->bytes, &s) ||
-        !page_at(dp->indices[k], *dp, page_len, dst->bytes, &d))
-      return XFER_E_RANGE;
-    starts[k] = d;
-  }
-  std::sort(starts.begin(), starts.end());
-  for (uint64_t k = 1; k < n_pages; ++k)
-    if (starts[k] - starts[k - 1] < page_len) return XFER_E_OVERLAP;
-  const uint64_t need = xfer_pages_plan_bytes(n_pages);
-  if (n_pages && (!dev || !aligned16((uintptr_t)dev) || dev_bytes < need)) return XFER_E_INVAL;
-  const uint64_t half = up16(n_pages * sizeof(uint32_t));
-  if (n_pages) {
-    if (hipMemcpy(dev, sp->indices, n_pages * sizeof(uint32_t), hipMemcpyHostToDevice) != hipSuccess ||
-        hipMemcpy((uint8_t *)dev + half, dp->indices, n_pages * sizeof(uint32_t), hipMemcpyHostToDevice) !=
-            hipSuccess)
-      return XFER_E_DEVICE;
-  }
-  xfer_pages_plan p;
-  std::memset(&p, 0, sizeof(p));
-  p.dev = dev;
-  p.dev_bytes = dev_bytes;
-  p.n_pages = n_pages;
-  p.page_len = page_len;
-  p.src_base = src->base + sp->offset;
-  p.src_stride = sp->stride;
-  p.dst_base = dst->base + dp->offset;
-  p.dst_stride = dp->stride;
-  p.off_src_idx = 0;
-  p.off_dst_idx = half;
-  p.units_per_page = (uint32_t)upp;
-  p.magic = kPagesMagic;
-  *out = p;
-  return XFER_OK;
+  return xfer::guarded([&]() -> int {
+    if (!out || !src || !dst || !sp || !dp) return XFER_E_INVAL;
+    if (n_pages && (!sp->indices || !dp->indices)) return XFER_E_INVAL;
+    if (page_len == 0 || !aligned16(page_len)) return XFER_E_INVAL;
+    if (!aligned16(sp->stride) || !aligned16(sp->offset) || !aligned16(dp->stride) || !aligned16(dp->offset))
+      return XFER_E_INVAL;
+    if (!aligned16(src->base) || !aligned16(dst->base)) return XFER_E_INVAL;
+    if (src->base > UINT64_MAX - src->bytes || dst->base > UINT64_MAX - dst->bytes) return XFER_E_INVAL;
+    if (src->base < dst->base + dst->bytes && dst->base < src->base + src->bytes) return XFER_E_INVAL;
+    const uint64_t upp = (page_len + xfer::kPageUnitBytes - 1) / xfer::kPageUnitBytes;
+    if (upp > UINT32_MAX || (n_pages && n_pages > UINT32_MAX / upp)) return XFER_E_UNSUPPORTED;
+    const uint64_t n_units = n_pages * upp;
+    if (xfer::paired_pieces(n_units) > xfer::kMaxGridBlocks) return XFER_E_UNSUPPORTED;
+    std::vector<uint64_t> starts(n_pages);
+    for (uint64_t k = 0; k < n_pages; ++k) {
+      uint64_t s, d;
+      if (!page_at(sp->indices[k], *sp, page_len, src->bytes, &s) ||
+          !page_at(dp->indices[k], *dp, page_len, dst->bytes, &d))
+        return XFER_E_RANGE;
+      starts[k] = d;
+    }
+    std::sort(starts.begin(), starts.end());
+    for (uint64_t k = 1; k < n_pages; ++k)
+      if (starts[k] - starts[k - 1] < page_len) return XFER_E_OVERLAP;
+    const uint64_t need = xfer_pages_plan_bytes(n_pages);
+    if (n_pages && (!dev || !aligned16((uintptr_t)dev) || dev_bytes < need)) return XFER_E_INVAL;
+    const uint64_t half = up16(n_pages * sizeof(uint32_t));
+    if (n_pages) {
+      if (hipMemcpy(dev, sp->indices, n_pages * sizeof(uint32_t), hipMemcpyHostToDevice) != hipSuccess ||
+          hipMemcpy((uint8_t *)dev + half, dp->indices, n_pages * sizeof(uint32_t), hipMemcpyHostToDevice) !=
+              hipSuccess)
+        return XFER_E_DEVICE;
+    }
+    xfer_pages_plan p;
+    std::memset(&p, 0, sizeof(p));
+    p.dev = dev;
+    p.dev_bytes = dev_bytes;
+    p.n_pages = n_pages;
+    p.page_len = page_len;
+    p.src_base = src->base + sp->offset;
+    p.src_stride = sp->stride;
+    p.dst_base = dst->base + dp->offset;
+    p.dst_stride = dp->stride;
+    p.off_src_idx = 0;
+    p.off_dst_idx = half;
+    p.units_per_page = (uint32_t)upp;
+    p.magic = kPagesMagic;
+    *out = p;
+    return XFER_OK;
+  });
 }
 
 int xfer_paged_copy(const xfer_pages_plan *plan, hipStream_t stream) {

@@ -15,10 +15,16 @@
  *   - Pointers marked (device) are device addresses of the GPU that is current
  *     on the calling thread; pointers marked (host) are host memory.  The
  *     caller owns every buffer, including the run plans; the library keeps no
- *     global state and allocates nothing.
- *   - Hot calls (pack, combine, argmax, gather, scatter) only enqueue work on
- *     `stream`: they never allocate, never synchronise and never block.
- *     xfer_runs_prepare is the one blocking set-up call.
+ *     global state and allocates no device memory.
+ *   - Hot calls (pack, combine, argmax, gather, scatter, the descriptor and
+ *     paged copies) only enqueue work on `stream`: they never allocate, never
+ *     synchronise and never block.  The set-up calls that upload a plan
+ *     (xfer_runs_prepare, xfer_descs_prepare, xfer_pages_prepare) block.
+ *   - The set-up calls that sort or expand a table on the host
+ *     (xfer_runs_validate, xfer_runs_prepare, xfer_groups_plan,
+ *     xfer_descs_prepare, xfer_pages_prepare) use temporary host memory and
+ *     return XFER_E_HOST_MEMORY when it cannot be allocated: no C++
+ *     exception ever leaves the library.
  *   - Every call checks all its arguments on the host first.  On any status
  *     other than XFER_OK and XFER_E_DEVICE nothing has been enqueued and no
  *     output byte has been written.  XFER_E_DEVICE reports a launch or copy
@@ -56,7 +62,9 @@ enum {
   XFER_E_RANGE = 4,       /* a segment outside the declared regions, or an
                              address computation that overflows 64 bits       */
   XFER_E_OVERLAP = 5,     /* destination segments overlap each other          */
-  XFER_E_DEVICE = 6       /* the HIP runtime refused a launch or a copy       */
+  XFER_E_DEVICE = 6,      /* the HIP runtime refused a launch or a copy       */
+  XFER_E_HOST_MEMORY = 7  /* a set-up call could not allocate its host scratch
+                             (no C++ exception ever leaves the library)       */
 };
 
 /* Static description of a status code (never NULL). */

@@ -3,6 +3,7 @@ header declares, and its host-side logic (argument checks, run-table
 validation and encoding, plan sizing) behaves as documented.  No call here
 reaches a kernel launch: every argument set either fails a host check or is
 empty work."""
+import ctypes
 import os
 import re
 
@@ -33,7 +34,7 @@ def test_library_exports_every_declared_call():
 
 
 def test_status_strings():
-    for s in range(7):
+    for s in range(8):
         assert x.status_str(s) and x.status_str(s) != "unknown status"
     assert x.status_str(99) == "unknown status"
 
@@ -275,3 +276,14 @@ def test_launch_size_limits():
     d = np.array([(big, 0, top)], x.DESC)
     st, _ = x.descs_prepare_status(d, 1 << 38, [(big, 1 << 38)], 0, 0)
     assert st == x.E_INVAL                                              # accepted up to the missing device buffer
+
+
+def test_setup_scratch_failure_is_a_status():
+    """A descriptor count whose host scratch cannot exist (2^60 entries of 16
+    bytes is past what a vector may hold) comes back as XFER_E_HOST_MEMORY,
+    before any descriptor is read; no C++ exception reaches the caller."""
+    d = np.zeros(1, x.DESC)
+    plan = x.DescsPlan()
+    st = x.lib().xfer_descs_prepare(d.ctypes.data, 1 << 60, 1 << 20, None, 0, None, 0, ctypes.byref(plan))
+    assert st == x.E_HOST_MEMORY
+    assert x.status_str(st) != "unknown status"
