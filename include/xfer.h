@@ -496,14 +496,20 @@ XFER_API int xfer_paged_copy(const xfer_pages_plan *plan, hipStream_t stream);
  *
  * The schedule is a list of operations, each on one of four streams
  * (compute 0, compute 1, wire 0, wire 1):
- *   PACK r c       compute r: wait SENT[r][s] of chunk c - R (slot free), pack, record PACKED[r][s]
+ *   PACK r c       compute r: wait SENT[r][s] of chunk c - R (slot free); for c < R also
+ *                             wait COMBINED[r][s] (the previous call's last reader of the slot,
+ *                             maybe on other streams); pack; record PACKED[r][s]
  *   WIRE r c       wire r:    wait PACKED[r][s]; wait COMBINED[1-r][s] of chunk c - R (peer slot free);
  *                             copy send[r] slot s -> recv[1-r] slot s; record SENT[r][s]
  *   COMBINE r c    compute r: wait SENT[1-r][s]; combine; record COMBINED[r][s]
- * with s = c mod R.  Every wait is always issued: the events are created
- * already recorded and complete (xfer_events_create), so the first R chunks
- * of a call either proceed at once or wait for the previous call that used
- * the same events and rings.  xfer_allreduce2_schedule returns the list (host
+ * with s = c mod R.  The events are created already recorded and complete
+ * (xfer_events_create), so the first R chunks of a call either proceed at
+ * once or wait for the previous call that used the same events and rings.
+ * With R >= 2, from chunk R on the slot-free waits (PACK's, WIRE's
+ * COMBINED) are left out: stream order and the waits of chunk c - 1 already
+ * order them (PACK r c follows COMBINE r c-1, which follows the peer's copy of
+ * chunk c-1, which follows the peer's pack of chunk c-1 and so the peer's
+ * earlier combines and copies).  Each operation keeps its record.  xfer_allreduce2_schedule returns the list (host
  * only, no GPU), so the ordering can be checked without running it.
  */
 enum { XFER_OP_PACK = 0, XFER_OP_WIRE = 1, XFER_OP_COMBINE = 2 };

@@ -103,6 +103,35 @@ def test_back_to_back_calls_reuse_rings_and_events():
         assert np.array_equal(down(outs[k][1], np.uint16), want), k
 
 
+@pytest.mark.parametrize("R", [1, 2])
+def test_later_call_on_other_streams_waits_for_the_earlier_readers(R):
+    """Two calls share rings and events but not streams, and nothing else
+    orders them.  The first is one chunk whose rank-1 wire stream starts with
+    a spin, so its rank-0 combine reads send[0] slot 0 about a millisecond
+    after its own copy out of that slot is done.  The second call's pack of
+    chunk 0 must wait for that combine, not only for the copy, or the first
+    call sums the second call's data."""
+    n, chunk = 100, 256                           # 128 elements per chunk: one chunk
+    first = Pair(n, chunk, R, x.OUT_F32)
+    second = Pair(n, chunk, R, x.OUT_F32)
+    second.send, second.recv, second.events = first.send, first.recv, first.events
+    ins = [(dg.normal_f32(n, 500 + 10 * k + R, 1.0), dg.normal_f32(n, 600 + 10 * k + R, 1.0)) for k in range(2)]
+    dev = [(up(a), up(b)) for a, b in ins]
+    outs = [[zeros(n * 4) for _ in range(2)] for _ in range(2)]
+    torch.cuda.synchronize()
+    with torch.cuda.stream(first.wire[1]):
+        torch.cuda._sleep(SPIN)
+    say("streamed later call on other streams, R", R)
+    for k, p in enumerate((first, second)):
+        st = x.allreduce2_streamed(dev[k], p.send, p.recv, outs[k], chunk, x.OUT_F32, p.compute, p.wire, p.events)
+        assert st == x.OK, x.status_str(st)
+    torch.cuda.synchronize()
+    for k, (a, b) in enumerate(ins):
+        want = _want(a, b, x.OUT_F32)
+        assert np.array_equal(down(outs[k][0], np.uint32), want), k
+        assert np.array_equal(down(outs[k][1], np.uint32), want), k
+
+
 def test_prompt_batch_2048x5120_two_512k_slots():
     n = 2048 * 5120
     a = dg.prompt_partial(n, dg.seed_for(2, 0, 2048))

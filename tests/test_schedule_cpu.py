@@ -177,3 +177,71 @@ def test_graph_builder_argument_checks():
     no_events = x.AllReduce2Desc.from_buffer_copy(d)
     no_events.events = None
     assert x.lib().xfer_allreduce2_streamed(ctypes.byref(no_events)) == x.E_INVAL
+
+
+def _accesses_call(op, call):
+    """As _accesses, with each call writing its own outputs (rings are shared)."""
+    out = []
+    for (name, r, k), w in _accesses(op):
+        out.append(((name, r, k, call) if name == "out" else (name, r, k), w))
+    return out
+
+
+def _two_calls(n1, n2, R, same_streams):
+    """Two calls on the same rings and events, the second on the same four
+    streams or on four others."""
+    a = x.allreduce2_schedule(n1, R)
+    b = x.allreduce2_schedule(n2, R)
+    ops = [dict(o, call=0) for o in a]
+    ops += [dict(o, call=1, stream=o["stream"] + (0 if same_streams else 4)) for o in b]
+    return ops
+
+
+def _hazards_calls(ops):
+    hb = _happens_before(ops)
+    acc = [_accesses_call(o, o["call"]) for o in ops]
+    bad = []
+    for j in range(len(ops)):
+        for i in range(j):
+            for (bi, wi), (bj, wj) in itertools.product(acc[i], acc[j]):
+                if bi == bj and (wi or wj) and i not in hb[j]:
+                    bad.append((i, j, bi))
+    return bad
+
+
+@pytest.mark.parametrize("R", [1, 2, 3])
+@pytest.mark.parametrize("n1,n2", [(1, 1), (2, 3), (5, 4), (7, 7)])
+@pytest.mark.parametrize("same_streams", [True, False])
+def test_a_later_call_is_ordered_after_the_earlier_one(R, n1, n2, same_streams):
+    """Rings and events shared by consecutive calls: every slot conflict
+    between the two calls is ordered, also when the second call runs on other
+    streams (then only the events order it)."""
+    assert _hazards_calls(_two_calls(n1, n2, R, same_streams)) == []
+
+
+@pytest.mark.parametrize("R", [1, 2, 3, 4])
+def test_every_wait_inside_a_call_is_load_bearing(R):
+    """No redundant waits: dropping any wait on an event recorded earlier in
+    the same call exposes a conflict (each costs host time in the runtime)."""
+    ops = x.allreduce2_schedule(3 * R + 2, R)
+    recorded = set()
+    checked = 0
+    for idx, op in enumerate(ops):
+        for e in op["waits"]:
+            if e in recorded:
+                assert _hazards(_without_wait(ops, idx, e)), (idx, op, e)
+                checked += 1
+        recorded.add(op["record"])
+    assert checked >= 2 * (3 * R + 2) - 2
+
+
+def test_waits_per_operation():
+    """With two slots, from chunk 2 on: pack none, wire one, combine one."""
+    R = 2
+    ops = x.allreduce2_schedule(6, R)
+    for o in ops:
+        n = len(o["waits"])
+        if o["chunk"] < R:
+            assert n == {x.OP_PACK: 2, x.OP_WIRE: 2, x.OP_COMBINE: 1}[o["kind"]], o
+        else:
+            assert n == {x.OP_PACK: 0, x.OP_WIRE: 1, x.OP_COMBINE: 1}[o["kind"]], o
