@@ -415,7 +415,7 @@ def cpu_baseline(w, budget_s=12.0):
     if w.seg_plan is not None:
         seg_t = oracle.RunTable(w.seg_table.runs_per_lane, w.seg_table.run_base, w.seg_table.run_stride,
                                 w.seg_table.run_count, w.n_blocks)
-    reps, t_total = 0, 0.0
+    reps, t_total, per_step = 0, 0.0, []
     while t_total < budget_s and reps < 50:
         t0 = time.perf_counter()
         oracle.pack(w.a_host, ring_a.size, ce, 0, w.n_chunks, ring=ring_a)
@@ -426,16 +426,31 @@ def cpu_baseline(w, budget_s=12.0):
         oracle.scatter(dst_t, w.seg, dst_regions, staging)
         oracle.argmax_merge(w.logits_host, SPLIT, 1)
         oracle.combine2(ring_a[:n], ring_b[:n], 0)
-        t_total += time.perf_counter() - t0
+        per_step.append(time.perf_counter() - t0)
+        t_total += per_step[-1]
         reps += 1
+    med = sorted(per_step)[len(per_step) // 2]
     return {
-        "value": round(step_bytes * reps / t_total / 1e9, 3),
+        "value": round(step_bytes / med / 1e9, 3),
         "unit": "GB/s",
         "cores": 1,
         "kind": "oracle",
         "sample": f"{reps} full steps of the same workload (same sizes and inputs), single-threaded C oracle, "
-                  f"{t_total:.1f} s; host has {os.cpu_count()} logical CPUs",
+                  f"{t_total:.1f} s in all, median step {med * 1e3:.1f} ms (value from the median); host: "
+                  f"{_cpu_model()}, {os.cpu_count()} logical CPUs",
     }
+
+
+def _cpu_model():
+    """The host CPU's model name, from /proc/cpuinfo (or 'unknown')."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 WORKLOADS = {
