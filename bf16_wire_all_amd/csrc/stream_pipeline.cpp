@@ -126,17 +126,27 @@ int xfer_allreduce2_schedule(uint32_t n_chunks, uint32_t R, xfer_op *ops, size_t
 
 int xfer_events_create(hipEvent_t *events, int n) {
   if (!events || n < 0) return XFER_E_INVAL;
+  // Slots start empty, so a failure releases exactly what this call created
+  // (a failed create may leave its slot untouched) and leaves every slot NULL.
+  for (int i = 0; i < n; ++i) events[i] = nullptr;
+  auto release = [&]() {
+    for (int j = 0; j < n; ++j)
+      if (events[j]) {
+        (void)hipEventDestroy(events[j]);
+        events[j] = nullptr;
+      }
+    return XFER_E_DEVICE;
+  };
   for (int i = 0; i < n; ++i) {
     // Recorded once and completed, so a first wait on it does not block.
-    if (hipEventCreateWithFlags(&events[i], hipEventDisableTiming) != hipSuccess ||
-        hipEventRecord(events[i], nullptr) != hipSuccess) {
-      for (int j = 0; j <= i; ++j)
-        if (events[j]) (void)hipEventDestroy(events[j]);
-      return XFER_E_DEVICE;
+    if (hipEventCreateWithFlags(&events[i], hipEventDisableTiming) != hipSuccess) {
+      events[i] = nullptr;
+      return release();
     }
+    if (hipEventRecord(events[i], nullptr) != hipSuccess) return release();
   }
   for (int i = 0; i < n; ++i)
-    if (hipEventSynchronize(events[i]) != hipSuccess) return XFER_E_DEVICE;
+    if (hipEventSynchronize(events[i]) != hipSuccess) return release();
   return XFER_OK;
 }
 

@@ -540,7 +540,9 @@ XFER_API int xfer_allreduce2_schedule(uint32_t n_chunks, uint32_t R, xfer_op *op
 
 /* Create n events without timing, each recorded once on the null stream and
  * completed before returning; destroy them.  Host resources for the driver
- * (set-up calls: they may block and allocate runtime objects). */
+ * (set-up calls: they may block and allocate runtime objects).  On
+ * XFER_E_DEVICE from xfer_events_create every event it created has been
+ * destroyed again and all n slots are NULL. */
 XFER_API int xfer_events_create(hipEvent_t *events, int n);
 XFER_API int xfer_events_destroy(hipEvent_t *events, int n);
 

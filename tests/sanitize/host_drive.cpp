@@ -1,0 +1,373 @@
+// Drives every exported call of libxfer's host code, built with the host
+// compiler against the mock HIP runtime, under AddressSanitizer and
+// UndefinedBehaviorSanitizer: valid and corrupted run tables, page lists,
+// descriptor lists and stream arguments from a seeded generator, plus
+// injected runtime failures.  The statuses are checked where the header
+// fixes them; everywhere else the point is that no call reads or writes out
+// of bounds, overflows a signed integer or leaks an event.
+#include <algorithm>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <numeric>
+#include <vector>
+
+#include "mock_hip.h"
+#include "xfer.h"
+
+#define CHECK(c)                                                            \
+  do {                                                                      \
+    if (!(c)) {                                                             \
+      std::fprintf(stderr, "CHECK failed: %s (line %d)\n", #c, __LINE__);  \
+      std::exit(1);                                                         \
+    }                                                                       \
+  } while (0)
+
+namespace {
+
+struct Rng {  // SplitMix64
+  uint64_t s;
+  uint64_t next() {
+    uint64_t z = (s += 0x9E3779B97F4A7C15ull);
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    return z ^ (z >> 31);
+  }
+  uint64_t below(uint64_t n) { return n ? next() % n : 0; }
+};
+
+// A host buffer standing in for device memory, 256-byte aligned.
+struct Buf {
+  uint8_t *p = nullptr;
+  size_t n = 0;
+  explicit Buf(size_t bytes) : n(bytes) {
+    const size_t cap = std::max<size_t>(256, (bytes + 255) / 256 * 256);
+    p = static_cast<uint8_t *>(std::aligned_alloc(256, cap));
+    std::memset(p, 0x5A, cap);
+  }
+  ~Buf() { std::free(p); }
+  Buf(const Buf &) = delete;
+  Buf &operator=(const Buf &) = delete;
+  uint64_t addr() const { return (uint64_t)(uintptr_t)p; }
+};
+
+hipStream_t token(uintptr_t k) { return reinterpret_cast<hipStream_t>(k); }
+
+void statuses() {
+  for (int s = -3; s < 12; ++s) CHECK(xfer_status_str(s) != nullptr);
+}
+
+void pack_combine(Rng &g) {
+  for (int it = 0; it < 400; ++it) {
+    const size_t n = g.below(3000);
+    const size_t chunk = 16 * (1 + g.below(8));
+    const size_t R = 1 + g.below(4);
+    Buf src(n * 4 + 16), ring(R * chunk);
+    const size_t ce = chunk / 2, n_chunks = n ? (n + ce - 1) / ce : 0;
+    const size_t b = g.below(n_chunks + 2), e = b + g.below(R + 2);
+    const int st = xfer_pack_bf16((const float *)src.p, n, (uint16_t *)ring.p, R * chunk, chunk, b, e, token(1));
+    if (n && b < e && e - b <= R && e <= n_chunks) CHECK(st == XFER_OK);
+    if (e - b > R) CHECK(st == XFER_E_INVAL);
+    // aliasing source and ring
+    CHECK(xfer_pack_bf16((const float *)ring.p, R * chunk / 4, (uint16_t *)ring.p, R * chunk, chunk, 0, 1,
+                         token(1)) == XFER_E_INVAL);
+    const int mode = (int)g.below(2);
+    Buf a(n * 2 + 16), bb(n * 2 + 16), out(n * 4 + 16), fa(n * 4 + 16), fb(n * 4 + 16);
+    CHECK(xfer_combine2((const uint16_t *)a.p, (const uint16_t *)bb.p, n, out.p, mode, token(2)) == XFER_OK);
+    if (mode == XFER_OUT_BF16)  // in place over rank 0's operand
+      CHECK(xfer_combine2((const uint16_t *)a.p, (const uint16_t *)bb.p, n, a.p, mode, token(2)) == XFER_OK);
+    CHECK(xfer_combine2_f32((const float *)fa.p, (const float *)fb.p, n, out.p, mode, token(2)) == XFER_OK);
+    if (n > 8)
+      CHECK(xfer_combine2((const uint16_t *)a.p, (const uint16_t *)bb.p, n, a.p + 16, mode, token(2)) ==
+            XFER_E_INVAL);
+    CHECK(xfer_combine2((const uint16_t *)a.p, (const uint16_t *)bb.p, n, out.p, 7, token(2)) == XFER_E_INVAL);
+  }
+}
+
+void argmax(Rng &g) {
+  for (int it = 0; it < 200; ++it) {
+    const uint32_t rows = 1 + (uint32_t)g.below(40);
+    const uint32_t n0 = 1 + (uint32_t)g.below(3000), n1 = 1 + (uint32_t)g.below(3000);
+    const uint32_t n0a = (n0 + 7) / 8 * 8;
+    const size_t ld = (n0a + n1 + g.below(4) * 8 + 7) / 8 * 8;
+    Buf m((size_t)rows * ld * 2);
+    xfer_shard s0{(const uint16_t *)m.p, ld, rows, n0, 0};
+    xfer_shard s1{(const uint16_t *)m.p + n0a, ld, rows, n1, n0};
+    const size_t wsb = xfer_argmax_workspace_bytes(rows, n0, n1);
+    Buf ws(wsb), out((size_t)rows * 16);
+    const int mode = (int)g.below(2);
+    CHECK(xfer_argmax_merge(&s0, &s1, mode, out.p, ws.p, wsb, token(3)) == XFER_OK);
+    CHECK(xfer_argmax_merge(&s0, &s1, mode, out.p, ws.p, wsb ? wsb - 1 : 0, token(3)) == XFER_E_INVAL);
+    xfer_shard clash = s1;
+    clash.col_offset = n0 - 1;  // overlaps shard 0's ids
+    CHECK(xfer_argmax_merge(&s0, &clash, mode, out.p, ws.p, wsb, token(3)) == XFER_E_INVAL);
+    CHECK(xfer_argmax_merge(&s0, &s1, mode, m.p, ws.p, wsb, token(3)) == XFER_E_INVAL);  // out over the logits
+  }
+}
+
+// Segment addresses [n_lanes][n_blocks] inside [base, base + slots * seg).
+std::vector<uint64_t> layout(Rng &g, uint32_t L, uint32_t B, uint64_t seg, uint64_t base, uint64_t slots,
+                             int kind) {
+  std::vector<uint64_t> a((size_t)L * B);
+  std::vector<uint64_t> perm(slots);
+  std::iota(perm.begin(), perm.end(), 0);
+  for (uint64_t i = slots; i > 1; --i) std::swap(perm[i - 1], perm[g.below(i)]);
+  for (uint32_t l = 0; l < L; ++l)
+    for (uint32_t b = 0; b < B; ++b) {
+      uint64_t s;
+      if (kind == 0) s = (uint64_t)b * L + l;             // block-major, dense
+      else if (kind == 1) s = (uint64_t)l * B + b;        // lane-major (one run per lane)
+      else if (kind == 2) s = perm[(uint64_t)l * B + b];  // shuffled, no repeats
+      else s = g.below(slots);                            // repeats allowed (sources only)
+      a[(size_t)l * B + b] = base + s * seg;
+    }
+  return a;
+}
+
+struct Table {
+  std::vector<uint32_t> rpl, count;
+  std::vector<uint64_t> base;
+  std::vector<int64_t> stride;
+  xfer_run_table t{};
+  void bind(uint32_t L, uint32_t B, uint64_t seg) {
+    t.n_lanes = L;
+    t.n_blocks = B;
+    t.seg_bytes = seg;
+    t.n_runs = base.size();
+    t.runs_per_lane = rpl.data();
+    t.run_base = base.data();
+    t.run_stride = stride.data();
+    t.run_count = count.data();
+  }
+};
+
+Table encode(const std::vector<uint64_t> &a, uint32_t L, uint32_t B, uint64_t seg, uint32_t max_count) {
+  Table T;
+  T.rpl.resize(L);
+  const uint64_t cap = (uint64_t)L * B;
+  T.base.resize(cap);
+  T.stride.resize(cap);
+  T.count.resize(cap);
+  uint64_t n = 0;
+  CHECK(xfer_runs_encode(a.data(), L, B, max_count, T.rpl.data(), T.base.data(), T.stride.data(), T.count.data(),
+                         cap, &n) == XFER_OK);
+  if (n) {
+    uint64_t small = 0;  // too little room is refused
+    CHECK(xfer_runs_encode(a.data(), L, B, max_count, T.rpl.data(), T.base.data(), T.stride.data(),
+                           T.count.data(), n - 1, &small) == XFER_E_RANGE);
+  }
+  T.base.resize(n);
+  T.stride.resize(n);
+  T.count.resize(n);
+  T.bind(L, B, seg);
+  return T;
+}
+
+void runs_and_groups(Rng &g) {
+  for (int it = 0; it < 300; ++it) {
+    const uint32_t L = 1 + (uint32_t)g.below(24), B = 1 + (uint32_t)g.below(40);
+    const uint64_t segs[] = {16, 48, 4096, 8192, 65536};
+    const uint64_t seg = segs[g.below(it % 7 == 0 ? 5 : 4)];
+    const uint64_t slots = (uint64_t)L * B + g.below(8);
+    Buf src(slots * seg), stg((uint64_t)L * B * seg), dst(slots * seg);
+    const int kind = (int)g.below(4);
+    const uint32_t max_count = (uint32_t)g.below(6);
+    const xfer_region sreg{src.addr(), src.n}, dreg{dst.addr(), dst.n};
+
+    Table S = encode(layout(g, L, B, seg, src.addr(), slots, kind), L, B, seg, max_count);
+    CHECK(xfer_runs_validate(&S.t, &sreg, 1, 0) == XFER_OK);
+    const size_t pb = xfer_runs_plan_bytes(&S.t);
+    Buf plan_dev(pb);
+    xfer_runs_plan sp;
+    CHECK(xfer_runs_prepare(&S.t, &sreg, 1, 0, plan_dev.p, pb, &sp) == XFER_OK);
+    CHECK(xfer_gather_runs(&sp, stg.p, stg.n, token(4)) == XFER_OK);
+    CHECK(xfer_gather_runs(&sp, stg.p, stg.n - 16, token(4)) == XFER_E_INVAL);
+    CHECK(xfer_scatter_runs(stg.p, stg.n, &sp, token(4)) == XFER_E_INVAL);  // a source plan
+
+    Table D = encode(layout(g, L, B, seg, dst.addr(), slots, kind == 3 ? 2 : kind), L, B, seg, max_count);
+    Buf dplan_dev(xfer_runs_plan_bytes(&D.t));
+    xfer_runs_plan dp;
+    CHECK(xfer_runs_prepare(&D.t, &dreg, 1, 1, dplan_dev.p, dplan_dev.n, &dp) == XFER_OK);
+    CHECK(xfer_scatter_runs(stg.p, stg.n, &dp, token(4)) == XFER_OK);
+    if (kind == 3 && (uint64_t)L * B > 1) {  // repeated slots as a destination
+      Table R = encode(layout(g, L, B, seg, dst.addr(), 1, 3), L, B, seg, max_count);
+      CHECK(xfer_runs_validate(&R.t, &dreg, 1, 1) == XFER_E_OVERLAP);
+    }
+
+    // the coalesced fetch of the source table
+    uint64_t nd = 0, slab = 0, ng = 0, ndense = 0;
+    std::vector<uint64_t> lb(S.t.n_runs + 1);
+    std::vector<int64_t> ls(S.t.n_runs + 1);
+    const uint64_t max_desc = 16 * (1 + g.below(4096));
+    const int st0 = xfer_groups_plan(&S.t, &sreg, 1, max_desc, nullptr, 0, &nd, &slab, lb.data(), ls.data(), &ng,
+                                     &ndense);
+    CHECK(st0 == XFER_E_RANGE || (st0 == XFER_OK && nd == 0));
+    std::vector<xfer_desc> descs(nd + 1);
+    CHECK(xfer_groups_plan(&S.t, &sreg, 1, max_desc, descs.data(), nd, &nd, &slab, lb.data(), ls.data(), &ng,
+                           &ndense) == XFER_OK);
+    CHECK(slab == (uint64_t)L * B * seg || kind == 3);
+    Buf ddev(xfer_descs_plan_bytes(nd)), slab_buf(slab);
+    xfer_descs_plan dplan;
+    CHECK(xfer_descs_prepare(descs.data(), nd, slab, &sreg, 1, ddev.p, ddev.n, &dplan) == XFER_OK);
+    CHECK(xfer_copy_descs(&dplan, slab_buf.p, slab, token(5)) == XFER_OK);
+    if (nd > 1) {
+      std::vector<xfer_desc> bad(descs.begin(), descs.begin() + nd);
+      bad[1].dst_off = bad[0].dst_off;  // two descriptors onto one slab range
+      CHECK(xfer_descs_prepare(bad.data(), nd, slab, &sreg, 1, ddev.p, ddev.n, &dplan) == XFER_E_OVERLAP);
+    }
+
+    // corrupted copies of the source table: any status, no undefined behaviour
+    for (int m = 0; m < 6; ++m) {
+      Table C = S;
+      C.bind(L, B, seg);
+      const uint64_t r = g.below(C.t.n_runs);
+      switch (m) {
+        case 0: C.count[r] = 0; break;
+        case 1: C.count[r] += 1; break;
+        case 2: C.base[r] += 8; break;
+        case 3: C.stride[r] = (int64_t)((g.next() & ~15ull) | 16u); break;
+        case 4: C.base[r] = ~0ull - 15; break;
+        case 5: C.rpl[g.below(L)] += 1; break;
+      }
+      if (m == 5) {  // the claimed run count must match the arrays' length
+        C.base.resize(C.t.n_runs + 1, src.addr());
+        C.stride.resize(C.t.n_runs + 1, 0);
+        C.count.resize(C.t.n_runs + 1, 1);
+        C.bind(L, B, seg);
+      }
+      const int v = xfer_runs_validate(&C.t, &sreg, 1, (int)(m & 1));
+      CHECK(v != XFER_OK || m == 3 || m == 2);
+      Buf cdev(xfer_runs_plan_bytes(&C.t));
+      xfer_runs_plan cp;
+      CHECK(xfer_runs_prepare(&C.t, &sreg, 1, 0, cdev.p, cdev.n, &cp) == v || m == 2 || m == 3);
+      uint64_t cnd = 0, cslab = 0;
+      std::vector<uint64_t> clb(C.t.n_runs + 1);
+      std::vector<int64_t> cls(C.t.n_runs + 1);
+      (void)xfer_groups_plan(&C.t, &sreg, 1, max_desc, nullptr, 0, &cnd, &cslab, clb.data(), cls.data(), nullptr,
+                             nullptr);
+    }
+  }
+}
+
+void pages(Rng &g) {
+  for (int it = 0; it < 300; ++it) {
+    const uint64_t page_len = 16 * (1 + g.below(it % 5 == 0 ? 1400 : 300));
+    const uint64_t n = g.below(200);
+    const uint64_t stride = page_len + 16 * g.below(4);
+    const uint64_t slots = n + g.below(16) + 1;
+    Buf src(slots * stride + 64), dst(slots * stride + 64);
+    std::vector<uint32_t> si(n + 1), di(n + 1);
+    std::vector<uint32_t> perm(slots);
+    std::iota(perm.begin(), perm.end(), 0u);
+    for (uint64_t i = slots; i > 1; --i) std::swap(perm[i - 1], perm[g.below(i)]);
+    for (uint64_t k = 0; k < n; ++k) {
+      si[k] = (uint32_t)g.below(slots);
+      di[k] = perm[k];
+    }
+    const int trouble = (int)g.below(5);  // 0: none, 1: dst repeat, 2: page out of range, 3: huge stride
+    if (trouble == 1 && n > 1) di[1] = di[0];
+    if (trouble == 2 && n) si[n - 1] = (uint32_t)slots;
+    const uint64_t sstride = trouble == 3 ? (1ull << 62) : stride;
+    const xfer_region sr{src.addr(), src.n}, dr{dst.addr(), dst.n};
+    const xfer_pages sp{si.data(), sstride, 16 * g.below(2)}, dp{di.data(), stride, 0};
+    Buf dev(xfer_pages_plan_bytes(n));
+    xfer_pages_plan plan;
+    const int st = xfer_pages_prepare(page_len, &sr, &sp, &dr, &dp, n, dev.p, dev.n, &plan);
+    if (n == 0) CHECK(st == XFER_OK);
+    if (trouble == 1 && n > 1) CHECK(st == XFER_E_OVERLAP);
+    if ((trouble == 2 || trouble == 3) && n) CHECK(st == XFER_E_RANGE);
+    if (st == XFER_OK) CHECK(xfer_paged_copy(&plan, token(6)) == XFER_OK);
+    if (trouble == 0 && n) {
+      mock::fail_memcpy_at((int)g.below(2));
+      CHECK(xfer_pages_prepare(page_len, &sr, &sp, &dr, &dp, n, dev.p, dev.n, &plan) == XFER_E_DEVICE);
+      mock::reset_failures();
+    }
+  }
+}
+
+void streamed(Rng &g) {
+  for (uint32_t R = 1; R <= 4; ++R)
+    for (uint32_t nc = 0; nc < 10; ++nc) {
+      std::vector<xfer_op> ops(6 * nc + 1);
+      size_t n_ops = 0;
+      CHECK(xfer_allreduce2_schedule(nc, R, ops.data(), ops.size(), &n_ops) == XFER_OK);
+      CHECK(n_ops == 6ull * nc);
+      for (size_t i = 0; i < n_ops; ++i) {
+        CHECK(ops[i].n_waits <= 2 && ops[i].record_event < 6 * R);
+        for (uint32_t w = 0; w < ops[i].n_waits; ++w) CHECK(ops[i].wait_event[w] < 6 * R);
+      }
+    }
+  // event creation with a failure at every position: nothing leaks, nothing
+  // that was not created is destroyed (the slots start as garbage)
+  for (int n = 1; n <= 6; ++n)
+    for (int k = 0; k < n; ++k) {
+      for (int which = 0; which < 2; ++which) {
+        std::vector<hipEvent_t> ev(n, reinterpret_cast<hipEvent_t>((uintptr_t)0xBAD0 + 16 * k));
+        if (which == 0) mock::fail_event_create_at(k);
+        else mock::fail_event_record_at(k);
+        CHECK(xfer_events_create(ev.data(), n) == XFER_E_DEVICE);
+        mock::reset_failures();
+        CHECK(mock::live_events() == 0);
+      }
+    }
+  for (int it = 0; it < 60; ++it) {
+    const uint64_t chunk = 16 * (1 + g.below(8));
+    const uint32_t R = 1 + (uint32_t)g.below(3);
+    const uint64_t n = g.below(2000);
+    const int mode = (int)g.below(2);
+    Buf s0(n * 4 + 16), s1(n * 4 + 16), snd0(R * chunk), snd1(R * chunk), rcv0(R * chunk), rcv1(R * chunk);
+    Buf o0(n * 4 + 16), o1(n * 4 + 16);
+    std::vector<hipEvent_t> ev(6 * R);
+    CHECK(xfer_events_create(ev.data(), (int)ev.size()) == XFER_OK);
+    xfer_allreduce2_desc d{};
+    d.src[0] = (const float *)s0.p;
+    d.src[1] = (const float *)s1.p;
+    d.send[0] = (uint16_t *)snd0.p;
+    d.send[1] = (uint16_t *)snd1.p;
+    d.recv[0] = (uint16_t *)rcv0.p;
+    d.recv[1] = (uint16_t *)rcv1.p;
+    d.out[0] = o0.p;
+    d.out[1] = o1.p;
+    d.n = n;
+    d.chunk_bytes = chunk;
+    d.ring_bytes = R * chunk;
+    d.out_mode = mode;
+    d.compute[0] = token(11);
+    d.compute[1] = token(12);
+    d.wire[0] = token(13);
+    d.wire[1] = token(14);
+    d.events = ev.data();
+    CHECK(xfer_allreduce2_streamed(&d) == XFER_OK);
+    CHECK(xfer_allreduce2_streamed(&d) == XFER_OK);  // a second call on the same rings and events
+    hipGraphExec_t ex = reinterpret_cast<hipGraphExec_t>((uintptr_t)1);
+    CHECK(xfer_allreduce2_graph_create(&d, &ex) == (n ? XFER_E_UNSUPPORTED : XFER_OK));
+    CHECK(ex == nullptr);
+    d.recv[1] = d.send[0];  // rings that alias
+    CHECK(xfer_allreduce2_streamed(&d) == (n ? XFER_E_INVAL : XFER_OK));
+    CHECK(xfer_events_destroy(ev.data(), (int)ev.size()) == XFER_OK);
+    CHECK(mock::live_events() == 0);
+  }
+  CHECK(xfer_allreduce2_graph_launch(nullptr, token(1)) == XFER_OK);
+  CHECK(xfer_allreduce2_graph_destroy(nullptr) == XFER_OK);
+}
+
+void host_memory() {
+  xfer_desc d{};
+  xfer_descs_plan plan;
+  CHECK(xfer_descs_prepare(&d, 1ull << 60, 1 << 20, nullptr, 0, nullptr, 0, &plan) == XFER_E_HOST_MEMORY);
+}
+
+}  // namespace
+
+int main() {
+  Rng g{0x5EED5A5Eull};
+  statuses();
+  pack_combine(g);
+  argmax(g);
+  runs_and_groups(g);
+  pages(g);
+  streamed(g);
+  host_memory();
+  std::printf("host code under sanitizers: %ld launches recorded, all checks passed\n", mock::g_launches);
+  return 0;
+}

@@ -1,0 +1,188 @@
+// The mock HIP runtime (mock_hip/hip/hip_runtime_api.h) and stand-ins for the
+// kernel launchers of libxfer's .hip files, for the sanitizer build of the
+// library's host code.  Launchers record what they were asked to launch and
+// touch the buffers they were given at their first and last byte, so a
+// wrong size or pointer handed to a launch shows up under the sanitizers.
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <set>
+
+#include "internal.h"
+#include "mock_hip.h"
+
+namespace {
+std::set<hipEvent_t> g_events;
+int g_create_calls = 0;
+int g_fail_create_at = -1;   // the create call (0-based) that fails, -1 none
+int g_record_calls = 0;
+int g_fail_record_at = -1;
+int g_memcpy_calls = 0;
+int g_fail_memcpy_at = -1;
+
+[[noreturn]] void die(const char *what) {
+  std::fprintf(stderr, "mock hip: %s\n", what);
+  std::abort();
+}
+
+void check_event(hipEvent_t e) {
+  if (!g_events.count(e)) die("unknown or destroyed event");
+}
+}  // namespace
+
+namespace mock {
+LaunchLog g_last;
+long g_launches = 0;
+
+void reset_failures() { g_fail_create_at = g_fail_record_at = g_fail_memcpy_at = -1; g_create_calls = g_record_calls = g_memcpy_calls = 0; }
+void fail_event_create_at(int k) { g_create_calls = 0; g_fail_create_at = k; }
+void fail_event_record_at(int k) { g_record_calls = 0; g_fail_record_at = k; }
+void fail_memcpy_at(int k) { g_memcpy_calls = 0; g_fail_memcpy_at = k; }
+size_t live_events() { return g_events.size(); }
+}  // namespace mock
+
+extern "C" {
+
+hipError_t hipMemcpy(void *dst, const void *src, size_t bytes, hipMemcpyKind kind) {
+  if (g_memcpy_calls++ == g_fail_memcpy_at) return hipErrorOutOfMemory;
+  if (kind != hipMemcpyHostToDevice) die("unexpected copy kind");
+  if (bytes && (!dst || !src)) die("NULL copy operand");
+  if (bytes) std::memcpy(dst, src, bytes);
+  return hipSuccess;
+}
+
+hipError_t hipMemcpyAsync(void *dst, const void *src, size_t bytes, hipMemcpyKind kind, hipStream_t) {
+  if (kind != hipMemcpyDeviceToDevice) die("unexpected async copy kind");
+  if (bytes && (!dst || !src)) die("NULL copy operand");
+  if (bytes) std::memmove(dst, src, bytes);
+  return hipSuccess;
+}
+
+hipError_t hipEventCreateWithFlags(hipEvent_t *event, unsigned) {
+  if (!event) die("NULL event slot");
+  if (g_create_calls++ == g_fail_create_at) return hipErrorOutOfMemory;  // leaves *event as it was
+  hipEvent_t e = reinterpret_cast<hipEvent_t>(std::malloc(16));
+  g_events.insert(e);
+  *event = e;
+  return hipSuccess;
+}
+
+hipError_t hipEventDestroy(hipEvent_t event) {
+  check_event(event);
+  g_events.erase(event);
+  std::free(event);
+  return hipSuccess;
+}
+
+hipError_t hipEventRecord(hipEvent_t event, hipStream_t) {
+  check_event(event);
+  if (g_record_calls++ == g_fail_record_at) return hipErrorInvalidValue;
+  return hipSuccess;
+}
+
+hipError_t hipEventSynchronize(hipEvent_t event) {
+  check_event(event);
+  return hipSuccess;
+}
+
+hipError_t hipStreamWaitEvent(hipStream_t, hipEvent_t event, unsigned) {
+  check_event(event);
+  return hipSuccess;
+}
+
+hipError_t hipGraphLaunch(hipGraphExec_t, hipStream_t) { die("graph launch reached"); }
+hipError_t hipGraphExecDestroy(hipGraphExec_t) { die("graph destroy reached"); }
+
+}  // extern "C"
+
+hipError_t hipLaunchKernel(const void *, dim3, dim3, void **, size_t, hipStream_t) { die("direct kernel launch"); }
+
+// ---- stand-ins for the launchers defined next to the kernels
+namespace {
+// Read the first and the last byte of [p, p + bytes): the sanitizers flag a
+// buffer that is smaller than the launch was told.
+uint8_t touch(const void *p, uint64_t bytes) {
+  if (!bytes) return 0;
+  const volatile uint8_t *b = static_cast<const volatile uint8_t *>(p);
+  return b[0] ^ b[bytes - 1];
+}
+void note(const char *name, uint64_t a, uint64_t b, uint64_t c) {
+  mock::g_last = mock::LaunchLog{name, a, b, c};
+  ++mock::g_launches;
+}
+}  // namespace
+
+namespace xfer {
+
+hipError_t launch_pack(const float *src, uint64_t n, uint16_t *ring, uint64_t ring_elems, uint64_t slot0,
+                       hipStream_t) {
+  if (slot0 >= ring_elems) die("pack: slot outside the ring");
+  touch(src, n * 4);
+  touch(ring, ring_elems * 2);
+  note("pack", n, ring_elems, slot0);
+  return hipSuccess;
+}
+
+hipError_t launch_combine(const uint16_t *a, const uint16_t *b, uint64_t n, void *out, int mode, hipStream_t) {
+  touch(a, n * 2);
+  touch(b, n * 2);
+  touch(out, n * (mode == XFER_OUT_F32 ? 4 : 2));
+  note("combine", n, (uint64_t)mode, 0);
+  return hipSuccess;
+}
+
+hipError_t launch_combine_f32(const float *a, const float *b, uint64_t n, void *out, int mode, hipStream_t) {
+  touch(a, n * 4);
+  touch(b, n * 4);
+  touch(out, n * (mode == XFER_OUT_F32 ? 4 : 2));
+  note("combine_f32", n, (uint64_t)mode, 0);
+  return hipSuccess;
+}
+
+uint32_t argmax_splits(uint32_t rows, uint32_t ncols0, uint32_t ncols1) {
+  (void)ncols0;
+  (void)ncols1;
+  return rows > 512 ? 1 : 4;
+}
+
+uint64_t argmax_workspace_bytes(uint32_t rows, uint32_t splits) { return (uint64_t)rows * 2 * splits * 8; }
+
+hipError_t launch_argmax(ArgmaxShard s0, ArgmaxShard s1, uint32_t rows, int mode, void *out, void *workspace,
+                         uint32_t splits, hipStream_t) {
+  for (const ArgmaxShard &s : {s0, s1}) touch(s.ptr, ((uint64_t)(rows - 1) * s.ld + s.ncols) * 2);
+  touch(out, (uint64_t)rows * (mode == XFER_ARGMAX ? 8 : 16));
+  touch(workspace, argmax_workspace_bytes(rows, splits));
+  note("argmax", rows, (uint64_t)mode, splits);
+  return hipSuccess;
+}
+
+hipError_t launch_gather(const PlanView &p, void *staging, hipStream_t) {
+  touch(staging, (uint64_t)p.n_lanes * p.n_blocks * p.seg_bytes);
+  touch(p.run_stride, 8);
+  note("gather", p.n_lanes, p.n_blocks, p.pieces);
+  return hipSuccess;
+}
+
+hipError_t launch_scatter(const PlanView &p, const void *staging, hipStream_t) {
+  touch(staging, (uint64_t)p.n_lanes * p.n_blocks * p.seg_bytes);
+  touch(p.run_stride, 8);
+  note("scatter", p.n_lanes, p.n_blocks, p.pieces);
+  return hipSuccess;
+}
+
+hipError_t launch_copy_descs(const xfer_desc *descs, uint64_t n_descs, uint32_t max_pieces, void *, hipStream_t) {
+  touch(descs, n_descs * sizeof(xfer_desc));
+  note("copy_descs", n_descs, max_pieces, 0);
+  return hipSuccess;
+}
+
+hipError_t launch_paged_copy(const PagesView &v, hipStream_t) {
+  const uint64_t n_pages = v.units_per_page ? v.n_units / v.units_per_page : 0;
+  touch(v.src_idx, n_pages * 4);
+  touch(v.dst_idx, n_pages * 4);
+  if (v.span == 0 || v.pieces == 0) die("paged copy: empty launch shape");
+  note("paged_copy", v.n_units, v.span, v.pieces);
+  return hipSuccess;
+}
+
+}  // namespace xfer
