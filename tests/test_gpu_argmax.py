@@ -16,11 +16,25 @@ pytestmark = pytest.mark.gpu
 MODES = ((x.ARGMAX, x.MAX_IDX), (x.TOP2, x.TOP2_REC))
 
 
+GUARD = 64  # guard bytes before and after the records, and after the workspace
+
+
+def _workspace(nbytes, value):
+    """A workspace of nbytes followed by a guard band."""
+    return filled(nbytes + GUARD, value), nbytes
+
+
 def _run(dl, s0, s1, rows, ws, mode, rec):
-    out = zeros(rows * rec.itemsize)
-    st = x.argmax_merge_raw(s0, s1, mode, out.data_ptr(), ws.data_ptr(), ws.numel())
+    ws_buf, ws_bytes = ws
+    ws_tail = down(ws_buf)[ws_bytes:].copy()
+    nb = rows * rec.itemsize
+    out = filled(GUARD + nb + GUARD, 0x5A)
+    st = x.argmax_merge_raw(s0, s1, mode, out.data_ptr() + GUARD, ws_buf.data_ptr(), ws_bytes)
     assert st == x.OK, x.status_str(st)
-    return down(out).view(rec)
+    got = down(out)
+    assert np.all(got[:GUARD] == 0x5A) and np.all(got[GUARD + nb:] == 0x5A), "write outside the records"
+    assert np.array_equal(down(ws_buf)[ws_bytes:], ws_tail), "write past the workspace"
+    return got[GUARD:GUARD + nb].copy().view(rec)
 
 
 def _check_matrix(logits, split, n1=None, calls=2):
@@ -32,7 +46,7 @@ def _check_matrix(logits, split, n1=None, calls=2):
     s0 = x.shard(dl.data_ptr(), cols, rows, split, 0)
     s1 = x.shard(dl.data_ptr() + 2 * split, cols, rows, n1, split)
     # the workspace needs no initialisation: start it full of garbage
-    ws = filled(x.argmax_workspace_bytes(rows, split, n1), 0xFF)
+    ws = _workspace(x.argmax_workspace_bytes(rows, split, n1), 0xFF)
     for mode, rec in MODES:
         want = oracle.argmax_merge(logits, split, mode, ncols1=n1)
         for _ in range(calls):
@@ -104,7 +118,7 @@ def test_odd_shapes(rows, n0, n1, pad, alphabet):
     s1 = x.shard(dl.data_ptr() + 2 * n0a, ld, rows, n1, n0)
     o0 = oracle.Shard(m.ctypes.data, ld, rows, n0, 0)
     o1 = oracle.Shard(m.ctypes.data + 2 * n0a, ld, rows, n1, n0)
-    ws = zeros(x.argmax_workspace_bytes(rows, n0, n1))
+    ws = _workspace(x.argmax_workspace_bytes(rows, n0, n1), 0)
     for mode, rec in MODES:
         want = oracle.argmax_merge_shards(o0, o1, mode)
         got = _run(dl, s0, s1, rows, ws, mode, rec)
