@@ -441,6 +441,38 @@ def cpu_baseline(w, budget_s=12.0):
     }
 
 
+# hipDeviceAttribute_t values (ROCm 7.x hip_runtime_api.h): peak core clock,
+# peak memory clock (both kHz) and compute-unit count.  The unit count is
+# compared with torch's to confirm the numbering before the clocks are used.
+_ATTR_CLOCK, _ATTR_MEM_CLOCK, _ATTR_CUS = 5, 60, 63
+
+
+def device_info():
+    """Name, architecture, compute units, memory and peak clocks of cuda:0."""
+    import ctypes
+
+    import torch
+
+    p = torch.cuda.get_device_properties(0)
+    info = {"name": p.name, "arch": getattr(p, "gcnArchName", None), "compute_units": p.multi_processor_count,
+            "memory_GiB": round(p.total_memory / 2**30, 1), "l2_bytes": getattr(p, "L2_cache_size", None),
+            "peak_clock_MHz": None, "peak_memory_clock_MHz": None}
+    try:
+        hip = ctypes.CDLL("libamdhip64.so")
+        v = ctypes.c_int(0)
+
+        def attr(a):
+            return v.value if hip.hipDeviceGetAttribute(ctypes.byref(v), a, 0) == 0 else None
+
+        if attr(_ATTR_CUS) == p.multi_processor_count:
+            clk, mem = attr(_ATTR_CLOCK), attr(_ATTR_MEM_CLOCK)
+            info["peak_clock_MHz"] = clk // 1000 if clk else None
+            info["peak_memory_clock_MHz"] = mem // 1000 if mem else None
+    except OSError:
+        pass
+    return info
+
+
 def _cpu_model():
     """The host CPU's model name, from /proc/cpuinfo (or 'unknown')."""
     try:
@@ -578,7 +610,10 @@ def main():
             "step_bytes": step_bytes,
             "parallelism": "single GPU; both ranks emulated in one HBM",
             "wire_dtype": "bf16",
+            "inputs": "seeded synthetic: xoshiro256** seeded by SplitMix64, seed 0x5EED0000 + config "
+                      "+ (rank << 8) + (label << 16)",
         },
+        "device": device_info(),
         "kernels": kernels,
         "pack_combine_GBps": (round((ab["pack_rank0"] + ab["pack_rank1"] + ab["combine_f32"]) /
                                     ((kms["pack_rank0"] + kms["pack_rank1"] + kms["combine_f32"]) * 1e-3) / 1e9, 1)
