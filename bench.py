@@ -78,6 +78,16 @@ def measured_traffic(kernel_file, key):
     return entry.get("traffic_bytes_per_launch")
 
 
+# Set from the command line: added to every input seed, and the ring slots
+# of the streamed all-reduce (two in the copy-engine design).
+SEED_OFFSET = 0
+SLOTS = 2
+
+
+def _seed(dg, *args):
+    return dg.seed_for(*args) + SEED_OFFSET
+
+
 class Workload:
     """Device buffers of one step, filled from the seeded generators.
 
@@ -101,8 +111,8 @@ class Workload:
         self.n_chunks = -(-n // (CHUNK // 2))
         log("bench: generating inputs")
         cfg = 5 if shuffled else 2
-        self.a_host = dg.prompt_partial(n, dg.seed_for(cfg, 0, tokens))
-        self.b_host = dg.prompt_partial(n, dg.seed_for(cfg, 1, tokens))
+        self.a_host = dg.prompt_partial(n, _seed(dg, cfg, 0, tokens))
+        self.b_host = dg.prompt_partial(n, _seed(dg, cfg, 1, tokens))
         self.a = torch.from_numpy(self.a_host).to(dev)
         self.b = torch.from_numpy(self.b_host).to(dev)
         # BF16 bit patterns are held in int16 tensors (2-byte elements)
@@ -110,7 +120,7 @@ class Workload:
         self.ring_b = torch.zeros(self.n_chunks * CHUNK // 2, dtype=torch.int16, device=dev)
         self.sum = torch.zeros(n, dtype=torch.float32, device=dev)
 
-        inp = dg.argmax_logits(ROWS, dg.seed_for(3))
+        inp = dg.argmax_logits(ROWS, _seed(dg, 3))
         self.logits_host = inp.logits
         self.logits = torch.from_numpy(inp.logits.view(np.int16).copy()).to(dev)
         p = self.logits.data_ptr()
@@ -123,12 +133,12 @@ class Workload:
         rb = dg.region_bytes_for(B, N_SLOTS, SG)
         self.regions = [torch.empty(rb, dtype=torch.uint8, device=dev) for _ in range(2)]
         bases = [r.data_ptr() for r in self.regions]
-        pos = dg.permutation(B, dg.seed_for(5, 0, 1)) if shuffled else None
+        pos = dg.permutation(B, _seed(dg, 5, 0, 1)) if shuffled else None
         self.src_addrs = dg.kv_src_addrs(B, N_SLOTS, SG, bases, pos=pos)
         self.region_hosts = []
         for i, r in enumerate(self.regions):
             h = np.empty(rb, np.uint8)
-            dg.fill_region(h, bases[i], self.src_addrs, SG, dg.seed_for(4, 0, i))
+            dg.fill_region(h, bases[i], self.src_addrs, SG, _seed(dg, 4, 0, i))
             r.copy_(torch.from_numpy(h))
             self.region_hosts.append(h)
         self.src_table = x.runs_encode(self.src_addrs, SG)
@@ -193,12 +203,12 @@ class Workload:
         self.streamed = streamed
         if streamed:
             # both ranks' rings and results, and four default-priority streams
-            self.send = [torch.zeros(2 * CHUNK // 2, dtype=torch.int16, device=dev) for _ in range(2)]
-            self.recv = [torch.zeros(2 * CHUNK // 2, dtype=torch.int16, device=dev) for _ in range(2)]
+            self.send = [torch.zeros(SLOTS * CHUNK // 2, dtype=torch.int16, device=dev) for _ in range(2)]
+            self.recv = [torch.zeros(SLOTS * CHUNK // 2, dtype=torch.int16, device=dev) for _ in range(2)]
             self.outs = [torch.zeros(n, dtype=torch.float32, device=dev) for _ in range(2)]
             self.compute = [torch.cuda.Stream(device=dev) for _ in range(2)]
             self.wire = [torch.cuda.Stream(device=dev) for _ in range(2)]
-            self.events = x.Events(6 * 2)
+            self.events = x.Events(6 * SLOTS)
         torch.cuda.synchronize()
 
     def _allreduce(self):
@@ -531,8 +541,8 @@ WORKLOADS = {
     },
     "streamed": {
         "args": {"tokens": TOKENS, "shuffled": False, "streamed": True},
-        "describe": "streamed two-rank all-reduce of two 2048x5120 F32 partials through 512 KiB BF16 chunks and two "
-                    "slots per rank: pack, device-to-device wire copy, F32 combine for both ranks, ordered by events "
+        "describe": "streamed two-rank all-reduce of two 2048x5120 F32 partials through 512 KiB BF16 chunks and "
+                    "config.slots ring slots per rank (two unless --slots says otherwise): pack, device-to-device wire copy, F32 combine for both ranks, ordered by events "
                     "on four streams (both ranks on one GPU)",
         "roofline_kernel": ("allreduce2_streamed", "allreduce2_streamed (40 chunks x 2 ranks x pack/copy/combine)",
                             None, None),
@@ -565,7 +575,13 @@ def main():
     ap.add_argument("--calib-copy", action="store_true", help="run only the copy used to scale PMC readings")
     ap.add_argument("--isolated", action="store_true",
                     help="also time each kernel alone and cold (1 GiB written between repetitions)")
+    ap.add_argument("--seed-offset", type=int, default=0, help="added to every input seed (default 0)")
+    ap.add_argument("--slots", type=int, default=2, help="ring slots of the streamed all-reduce (default 2)")
     args = ap.parse_args()
+    global SEED_OFFSET, SLOTS
+    SEED_OFFSET, SLOTS = args.seed_offset, args.slots
+    if SLOTS < 1:
+        sys.exit("--slots must be >= 1")
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}): the hot path here is single-GPU "
               "by design (both ranks are emulated in one HBM)", file=sys.stderr)
@@ -611,7 +627,8 @@ def main():
             "parallelism": "single GPU; both ranks emulated in one HBM",
             "wire_dtype": "bf16",
             "inputs": "seeded synthetic: xoshiro256** seeded by SplitMix64, seed 0x5EED0000 + config "
-                      "+ (rank << 8) + (label << 16)",
+                      f"+ (rank << 8) + (label << 16) + {SEED_OFFSET}",
+            **({"slots": SLOTS} if args.workload == "streamed" else {}),
         },
         "device": device_info(),
         "kernels": kernels,
