@@ -542,8 +542,9 @@ WORKLOADS = {
     "streamed": {
         "args": {"tokens": TOKENS, "shuffled": False, "streamed": True},
         "describe": "streamed two-rank all-reduce of two 2048x5120 F32 partials through 512 KiB BF16 chunks and "
-                    "config.slots ring slots per rank (two unless --slots says otherwise): pack, device-to-device wire copy, F32 combine for both ranks, ordered by events "
-                    "on four streams (both ranks on one GPU)",
+                    "config.slots ring slots per rank (two unless --slots says otherwise): pack, "
+                    "device-to-device wire copy, F32 combine for both ranks, ordered by events on four streams "
+                    "(both ranks on one GPU)",
         "roofline_kernel": ("allreduce2_streamed", "allreduce2_streamed (40 chunks x 2 ranks x pack/copy/combine)",
                             None, None),
     },
