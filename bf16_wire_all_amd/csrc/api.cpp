@@ -175,6 +175,8 @@ bool plan_ok(const xfer_runs_plan *p) {
   if (p->group_blocks == 0 || p->group_blocks > xfer::kMaxGroupBlocks || p->group_blocks % p->tile_blocks)
     return false;
   if (p->pieces == 0 || (p->seg_bytes / 16) % p->pieces || (p->pieces > 1 && p->tile_blocks != 1)) return false;
+  // a split segment's piece is whole 4 KiB units (the kernel pairs units)
+  if (p->pieces > 1 && (p->seg_bytes / 16 / p->pieces) % 256) return false;
   if (p->lanes_per_wg == 0 || p->lanes_per_wg > xfer::kMaxLanesPerWorkgroup) return false;
   if (p->off_run_stride + up16(p->n_runs * 8) > p->dev_bytes) return false;
   return true;

@@ -183,6 +183,13 @@ void runs_and_groups(Rng &g) {
     CHECK(xfer_gather_runs(&sp, stg.p, stg.n, token(4)) == XFER_OK);
     CHECK(xfer_gather_runs(&sp, stg.p, stg.n - 16, token(4)) == XFER_E_INVAL);
     CHECK(xfer_scatter_runs(stg.p, stg.n, &sp, token(4)) == XFER_E_INVAL);  // a source plan
+    if (sp.pieces > 1) {  // an edited plan whose pieces are not whole 4 KiB units is refused
+      xfer_runs_plan bad = sp;
+      bad.pieces = sp.pieces * 4;
+      CHECK(xfer_gather_runs(&bad, stg.p, stg.n, token(4)) == XFER_E_INVAL);
+      bad.pieces = sp.pieces * 2;  // one unit per piece: still whole units
+      CHECK(xfer_gather_runs(&bad, stg.p, stg.n, token(4)) == XFER_OK);
+    }
 
     Table D = encode(layout(g, L, B, seg, dst.addr(), slots, kind == 3 ? 2 : kind), L, B, seg, max_count);
     Buf dplan_dev(xfer_runs_plan_bytes(&D.t));
