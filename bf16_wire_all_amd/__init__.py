@@ -179,8 +179,9 @@ def _check(status: int, what: str) -> None:
 
 
 def _stream(stream):
+    """A torch stream or a raw hipStream_t handle; None is torch's current stream."""
     if stream is not None:
-        return int(stream)
+        return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
     import torch
     return torch.cuda.current_stream().cuda_stream
 
