@@ -82,6 +82,7 @@ def measured_traffic(kernel_file, key):
 # of the streamed all-reduce (two in the copy-engine design).
 SEED_OFFSET = 0
 SLOTS = 2
+STREAM_CHUNK = CHUNK  # BF16 bytes per chunk of the streamed all-reduce
 
 
 def _seed(dg, *args):
@@ -203,8 +204,8 @@ class Workload:
         self.streamed = streamed
         if streamed:
             # both ranks' rings and results, and four default-priority streams
-            self.send = [torch.zeros(SLOTS * CHUNK // 2, dtype=torch.int16, device=dev) for _ in range(2)]
-            self.recv = [torch.zeros(SLOTS * CHUNK // 2, dtype=torch.int16, device=dev) for _ in range(2)]
+            self.send = [torch.zeros(SLOTS * STREAM_CHUNK // 2, dtype=torch.int16, device=dev) for _ in range(2)]
+            self.recv = [torch.zeros(SLOTS * STREAM_CHUNK // 2, dtype=torch.int16, device=dev) for _ in range(2)]
             self.outs = [torch.zeros(n, dtype=torch.float32, device=dev) for _ in range(2)]
             self.compute = [torch.cuda.Stream(device=dev) for _ in range(2)]
             self.wire = [torch.cuda.Stream(device=dev) for _ in range(2)]
@@ -216,7 +217,7 @@ class Workload:
         cur = self.torch.cuda.current_stream()
         for s in self.compute + self.wire:
             s.wait_stream(cur)
-        st = self.x.allreduce2_streamed((self.a, self.b), self.send, self.recv, self.outs, CHUNK, self.x.OUT_F32,
+        st = self.x.allreduce2_streamed((self.a, self.b), self.send, self.recv, self.outs, STREAM_CHUNK, self.x.OUT_F32,
                                         self.compute, self.wire, self.events)
         if st != self.x.OK:
             raise RuntimeError(f"xfer_allreduce2_streamed: {self.x.status_str(st)}")
@@ -541,8 +542,9 @@ WORKLOADS = {
     },
     "streamed": {
         "args": {"tokens": TOKENS, "shuffled": False, "streamed": True},
-        "describe": "streamed two-rank all-reduce of two 2048x5120 F32 partials through 512 KiB BF16 chunks and "
-                    "config.slots ring slots per rank (two unless --slots says otherwise): pack, "
+        "describe": "streamed two-rank all-reduce of two 2048x5120 F32 partials through BF16 chunks of "
+                    "config.chunk_bytes (512 KiB unless --chunk-kib says otherwise) and config.slots ring slots "
+                    "per rank (two unless --slots says otherwise): pack, "
                     "device-to-device wire copy, F32 combine for both ranks, ordered by events on four streams "
                     "(both ranks on one GPU)",
         "roofline_kernel": ("allreduce2_streamed", "allreduce2_streamed (40 chunks x 2 ranks x pack/copy/combine)",
@@ -578,11 +580,15 @@ def main():
                     help="also time each kernel alone and cold (1 GiB written between repetitions)")
     ap.add_argument("--seed-offset", type=int, default=0, help="added to every input seed (default 0)")
     ap.add_argument("--slots", type=int, default=2, help="ring slots of the streamed all-reduce (default 2)")
+    ap.add_argument("--chunk-kib", type=int, default=CHUNK // 1024,
+                    help="chunk size of the streamed all-reduce in KiB of BF16 (default 512)")
     args = ap.parse_args()
-    global SEED_OFFSET, SLOTS
-    SEED_OFFSET, SLOTS = args.seed_offset, args.slots
+    global SEED_OFFSET, SLOTS, STREAM_CHUNK
+    SEED_OFFSET, SLOTS, STREAM_CHUNK = args.seed_offset, args.slots, args.chunk_kib * 1024
     if SLOTS < 1:
         sys.exit("--slots must be >= 1")
+    if args.chunk_kib < 1:
+        sys.exit("--chunk-kib must be >= 1")
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}): the hot path here is single-GPU "
               "by design (both ranks are emulated in one HBM)", file=sys.stderr)
@@ -629,7 +635,7 @@ def main():
             "wire_dtype": "bf16",
             "inputs": "seeded synthetic: xoshiro256** seeded by SplitMix64, seed 0x5EED0000 + config "
                       f"+ (rank << 8) + (label << 16) + {SEED_OFFSET}",
-            **({"slots": SLOTS} if args.workload == "streamed" else {}),
+            **({"slots": SLOTS, "chunk_bytes": STREAM_CHUNK} if args.workload == "streamed" else {}),
         },
         "device": device_info(),
         "kernels": kernels,
