@@ -358,6 +358,77 @@ void streamed(Rng &g) {
   CHECK(xfer_allreduce2_graph_destroy(nullptr) == XFER_OK);
 }
 
+// A launch the runtime refuses comes back as XFER_E_DEVICE from every hot call.
+void refused_launches() {
+  const size_t n = 1000;
+  Buf src(n * 4), ring(2 * 64), a(n * 2), b(n * 2), out(n * 4);
+  Buf m(16 * 64 * 2), ws(1 << 16), rec(16 * 16);
+  const uint32_t L = 4, B = 8;
+  const uint64_t seg = 64;
+  Buf reg(L * B * seg), stg(L * B * seg), dst(L * B * seg);
+  std::vector<uint64_t> addrs((size_t)L * B);
+  for (uint32_t l = 0; l < L; ++l)
+    for (uint32_t k = 0; k < B; ++k) addrs[(size_t)l * B + k] = reg.addr() + ((uint64_t)k * L + l) * seg;
+  Table T = encode(addrs, L, B, seg, 0);
+  const xfer_region sreg{reg.addr(), reg.n};
+  Buf pdev(xfer_runs_plan_bytes(&T.t));
+  xfer_runs_plan sp;
+  CHECK(xfer_runs_prepare(&T.t, &sreg, 1, 0, pdev.p, pdev.n, &sp) == XFER_OK);
+  for (auto &x : addrs) x = x - reg.addr() + dst.addr();
+  Table D = encode(addrs, L, B, seg, 0);
+  const xfer_region dreg{dst.addr(), dst.n};
+  Buf ddev(xfer_runs_plan_bytes(&D.t));
+  xfer_runs_plan dp;
+  CHECK(xfer_runs_prepare(&D.t, &dreg, 1, 1, ddev.p, ddev.n, &dp) == XFER_OK);
+  xfer_desc desc{reg.addr(), 0, reg.n};
+  Buf descdev(xfer_descs_plan_bytes(1));
+  xfer_descs_plan fp;
+  CHECK(xfer_descs_prepare(&desc, 1, stg.n, &sreg, 1, descdev.p, descdev.n, &fp) == XFER_OK);
+  std::vector<uint32_t> idx(L * B);
+  std::iota(idx.begin(), idx.end(), 0u);
+  const xfer_pages pl{idx.data(), seg, 0};
+  Buf pgdev(xfer_pages_plan_bytes(idx.size()));
+  xfer_pages_plan pp;
+  CHECK(xfer_pages_prepare(seg, &sreg, &pl, &dreg, &pl, idx.size(), pgdev.p, pgdev.n, &pp) == XFER_OK);
+  xfer_shard s0{(const uint16_t *)m.p, 64, 16, 32, 0}, s1{(const uint16_t *)m.p + 32, 64, 16, 32, 32};
+  std::vector<hipEvent_t> ev(12);
+  CHECK(xfer_events_create(ev.data(), 12) == XFER_OK);
+  xfer_allreduce2_desc d{};
+  Buf snd0(128), snd1(128), rcv0(128), rcv1(128), o0(n * 4), o1(n * 4), f1(n * 4);
+  d.src[0] = (const float *)src.p;
+  d.src[1] = (const float *)f1.p;
+  d.send[0] = (uint16_t *)snd0.p;
+  d.send[1] = (uint16_t *)snd1.p;
+  d.recv[0] = (uint16_t *)rcv0.p;
+  d.recv[1] = (uint16_t *)rcv1.p;
+  d.out[0] = o0.p;
+  d.out[1] = o1.p;
+  d.n = n;
+  d.chunk_bytes = 64;
+  d.ring_bytes = 128;
+  d.out_mode = XFER_OUT_F32;
+  d.compute[0] = token(21);
+  d.compute[1] = token(22);
+  d.wire[0] = token(23);
+  d.wire[1] = token(24);
+  d.events = ev.data();
+  mock::fail_launches(true);
+  CHECK(xfer_pack_bf16((const float *)src.p, n, (uint16_t *)ring.p, 128, 64, 0, 2, token(1)) == XFER_E_DEVICE);
+  CHECK(xfer_combine2((const uint16_t *)a.p, (const uint16_t *)b.p, n, out.p, XFER_OUT_F32, token(1)) == XFER_E_DEVICE);
+  CHECK(xfer_combine2_f32((const float *)src.p, (const float *)f1.p, n, out.p, XFER_OUT_BF16, token(1)) ==
+        XFER_E_DEVICE);
+  CHECK(xfer_argmax_merge(&s0, &s1, XFER_TOP2, rec.p, ws.p, ws.n, token(1)) == XFER_E_DEVICE);
+  CHECK(xfer_gather_runs(&sp, stg.p, stg.n, token(1)) == XFER_E_DEVICE);
+  CHECK(xfer_scatter_runs(stg.p, stg.n, &dp, token(1)) == XFER_E_DEVICE);
+  CHECK(xfer_copy_descs(&fp, stg.p, stg.n, token(1)) == XFER_E_DEVICE);
+  CHECK(xfer_paged_copy(&pp, token(1)) == XFER_E_DEVICE);
+  CHECK(xfer_allreduce2_streamed(&d) == XFER_E_DEVICE);
+  mock::reset_failures();
+  CHECK(xfer_allreduce2_streamed(&d) == XFER_OK);
+  CHECK(xfer_events_destroy(ev.data(), 12) == XFER_OK);
+  CHECK(mock::live_events() == 0);
+}
+
 void host_memory() {
   xfer_desc d{};
   xfer_descs_plan plan;
@@ -374,6 +445,7 @@ int main() {
   runs_and_groups(g);
   pages(g);
   streamed(g);
+  refused_launches();
   host_memory();
   std::printf("host code under sanitizers: %ld launches recorded, all checks passed\n", mock::g_launches);
   return 0;

@@ -19,6 +19,7 @@ int g_record_calls = 0;
 int g_fail_record_at = -1;
 int g_memcpy_calls = 0;
 int g_fail_memcpy_at = -1;
+bool g_fail_launches = false;
 
 [[noreturn]] void die(const char *what) {
   std::fprintf(stderr, "mock hip: %s\n", what);
@@ -34,7 +35,12 @@ namespace mock {
 LaunchLog g_last;
 long g_launches = 0;
 
-void reset_failures() { g_fail_create_at = g_fail_record_at = g_fail_memcpy_at = -1; g_create_calls = g_record_calls = g_memcpy_calls = 0; }
+void reset_failures() {
+  g_fail_create_at = g_fail_record_at = g_fail_memcpy_at = -1;
+  g_create_calls = g_record_calls = g_memcpy_calls = 0;
+  g_fail_launches = false;
+}
+void fail_launches(bool on) { g_fail_launches = on; }
 void fail_event_create_at(int k) { g_create_calls = 0; g_fail_create_at = k; }
 void fail_event_record_at(int k) { g_record_calls = 0; g_fail_record_at = k; }
 void fail_memcpy_at(int k) { g_memcpy_calls = 0; g_fail_memcpy_at = k; }
@@ -106,9 +112,11 @@ uint8_t touch(const void *p, uint64_t bytes) {
   const volatile uint8_t *b = static_cast<const volatile uint8_t *>(p);
   return b[0] ^ b[bytes - 1];
 }
-void note(const char *name, uint64_t a, uint64_t b, uint64_t c) {
+hipError_t note(const char *name, uint64_t a, uint64_t b, uint64_t c) {
+  if (g_fail_launches) return hipErrorInvalidValue;  // the runtime refuses the launch
   mock::g_last = mock::LaunchLog{name, a, b, c};
   ++mock::g_launches;
+  return hipSuccess;
 }
 }  // namespace
 
@@ -119,24 +127,21 @@ hipError_t launch_pack(const float *src, uint64_t n, uint16_t *ring, uint64_t ri
   if (slot0 >= ring_elems) die("pack: slot outside the ring");
   touch(src, n * 4);
   touch(ring, ring_elems * 2);
-  note("pack", n, ring_elems, slot0);
-  return hipSuccess;
+  return note("pack", n, ring_elems, slot0);
 }
 
 hipError_t launch_combine(const uint16_t *a, const uint16_t *b, uint64_t n, void *out, int mode, hipStream_t) {
   touch(a, n * 2);
   touch(b, n * 2);
   touch(out, n * (mode == XFER_OUT_F32 ? 4 : 2));
-  note("combine", n, (uint64_t)mode, 0);
-  return hipSuccess;
+  return note("combine", n, (uint64_t)mode, 0);
 }
 
 hipError_t launch_combine_f32(const float *a, const float *b, uint64_t n, void *out, int mode, hipStream_t) {
   touch(a, n * 4);
   touch(b, n * 4);
   touch(out, n * (mode == XFER_OUT_F32 ? 4 : 2));
-  note("combine_f32", n, (uint64_t)mode, 0);
-  return hipSuccess;
+  return note("combine_f32", n, (uint64_t)mode, 0);
 }
 
 uint32_t argmax_splits(uint32_t rows, uint32_t ncols0, uint32_t ncols1) {
@@ -152,28 +157,24 @@ hipError_t launch_argmax(ArgmaxShard s0, ArgmaxShard s1, uint32_t rows, int mode
   for (const ArgmaxShard &s : {s0, s1}) touch(s.ptr, ((uint64_t)(rows - 1) * s.ld + s.ncols) * 2);
   touch(out, (uint64_t)rows * (mode == XFER_ARGMAX ? 8 : 16));
   touch(workspace, argmax_workspace_bytes(rows, splits));
-  note("argmax", rows, (uint64_t)mode, splits);
-  return hipSuccess;
+  return note("argmax", rows, (uint64_t)mode, splits);
 }
 
 hipError_t launch_gather(const PlanView &p, void *staging, hipStream_t) {
   touch(staging, (uint64_t)p.n_lanes * p.n_blocks * p.seg_bytes);
   touch(p.run_stride, 8);
-  note("gather", p.n_lanes, p.n_blocks, p.pieces);
-  return hipSuccess;
+  return note("gather", p.n_lanes, p.n_blocks, p.pieces);
 }
 
 hipError_t launch_scatter(const PlanView &p, const void *staging, hipStream_t) {
   touch(staging, (uint64_t)p.n_lanes * p.n_blocks * p.seg_bytes);
   touch(p.run_stride, 8);
-  note("scatter", p.n_lanes, p.n_blocks, p.pieces);
-  return hipSuccess;
+  return note("scatter", p.n_lanes, p.n_blocks, p.pieces);
 }
 
 hipError_t launch_copy_descs(const xfer_desc *descs, uint64_t n_descs, uint32_t max_pieces, void *, hipStream_t) {
   touch(descs, n_descs * sizeof(xfer_desc));
-  note("copy_descs", n_descs, max_pieces, 0);
-  return hipSuccess;
+  return note("copy_descs", n_descs, max_pieces, 0);
 }
 
 hipError_t launch_paged_copy(const PagesView &v, hipStream_t) {
@@ -181,8 +182,7 @@ hipError_t launch_paged_copy(const PagesView &v, hipStream_t) {
   touch(v.src_idx, n_pages * 4);
   touch(v.dst_idx, n_pages * 4);
   if (v.span == 0 || v.pieces == 0) die("paged copy: empty launch shape");
-  note("paged_copy", v.n_units, v.span, v.pieces);
-  return hipSuccess;
+  return note("paged_copy", v.n_units, v.span, v.pieces);
 }
 
 }  // namespace xfer

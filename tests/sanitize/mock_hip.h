@@ -15,4 +15,5 @@ void fail_event_create_at(int k);  // the k-th event create from now fails (no h
 void fail_event_record_at(int k);
 void fail_memcpy_at(int k);
 size_t live_events();
+void fail_launches(bool on);       // every launcher returns an error while on
 }  // namespace mock
