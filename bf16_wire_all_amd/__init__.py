@@ -31,6 +31,7 @@ EXPORTED = [
     "xfer_groups_plan", "xfer_descs_plan_bytes", "xfer_descs_prepare", "xfer_copy_descs",
     "xfer_pages_plan_bytes", "xfer_pages_prepare", "xfer_paged_copy",
     "xfer_allreduce2_graph_create", "xfer_allreduce2_graph_launch", "xfer_allreduce2_graph_destroy",
+    "xfer_argmax_merge_noalloc",
 ]
 
 
@@ -119,6 +120,8 @@ def lib():
         L.xfer_argmax_workspace_bytes.restype = S
         L.xfer_argmax_merge.argtypes = [ctypes.POINTER(Shard), ctypes.POINTER(Shard), I, P, P, S, P]
         L.xfer_argmax_merge.restype = I
+        L.xfer_argmax_merge_noalloc.argtypes = [ctypes.POINTER(Shard), ctypes.POINTER(Shard), I, P, P]
+        L.xfer_argmax_merge_noalloc.restype = I
         L.xfer_runs_encode.argtypes = [P, U32, U32, U32, P, P, P, P, U64, ctypes.POINTER(U64)]
         L.xfer_runs_encode.restype = I
         L.xfer_runs_validate.argtypes = [ctypes.POINTER(RunTableC), ctypes.POINTER(Region), I, I]
@@ -269,6 +272,21 @@ def argmax_merge_raw(s0: Shard, s1: Shard, mode: int, out_ptr: int, ws_ptr: int,
                      stream=None) -> int:
     return lib().xfer_argmax_merge(ctypes.byref(s0), ctypes.byref(s1), mode, out_ptr, ws_ptr, ws_bytes,
                                    _stream(stream))
+
+
+# Bytes of the library's static partials array on each GPU (include/xfer.h).
+ARGMAX_SCRATCH_BYTES = 65536
+
+
+def argmax_merge_noalloc(s0: Shard, s1: Shard, mode: int, out, stream=None) -> None:
+    """argmax_merge without a workspace: the partial records go to the
+    library's static device array (calls that overlap on one GPU race)."""
+    _check(lib().xfer_argmax_merge_noalloc(ctypes.byref(s0), ctypes.byref(s1), mode, _dev(out), _stream(stream)),
+           "xfer_argmax_merge_noalloc")
+
+
+def argmax_merge_noalloc_raw(s0: Shard, s1: Shard, mode: int, out_ptr: int, stream=None) -> int:
+    return lib().xfer_argmax_merge_noalloc(ctypes.byref(s0), ctypes.byref(s1), mode, out_ptr, _stream(stream))
 
 
 # --------------------------------------------------------------- run tables

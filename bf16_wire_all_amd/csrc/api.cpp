@@ -296,15 +296,26 @@ size_t xfer_argmax_workspace_bytes(uint32_t rows, uint32_t ncols0, uint32_t ncol
   return (size_t)xfer::argmax_workspace_bytes(rows, xfer::argmax_splits(rows, ncols0, ncols1));
 }
 
-int xfer_argmax_merge(const xfer_shard *s0, const xfer_shard *s1, int mode, void *out, void *workspace,
-                      size_t workspace_bytes, hipStream_t stream) {
+namespace {
+
+// The checks xfer_argmax_merge and xfer_argmax_merge_noalloc share: shards,
+// mode and output.  On XFER_OK with rows > 0, fills the launch arguments,
+// the workspace bytes the call needs and the shards' byte spans.
+struct ArgmaxCall {
+  uint32_t rows = 0, splits = 0;
+  uint64_t need = 0;
+  uint64_t lo[2] = {0, 0}, span[2] = {0, 0};
+  xfer::ArgmaxShard a{}, b{};
+};
+
+int argmax_checks(const xfer_shard *s0, const xfer_shard *s1, int mode, const void *out, ArgmaxCall *c) {
   if (!s0 || !s1) return XFER_E_INVAL;
   if (mode != XFER_ARGMAX && mode != XFER_TOP2) return XFER_E_INVAL;
   if (s0->rows != s1->rows) return XFER_E_INVAL;
   const uint32_t rows = s0->rows;
+  c->rows = rows;
   if (rows == 0) return XFER_OK;
   const xfer_shard *s[2] = {s0, s1};
-  uint64_t lo[2], span[2];
   for (int i = 0; i < 2; ++i) {
     if (s[i]->ncols == 0) return XFER_E_INVAL;
     if ((uint64_t)s[i]->col_offset + s[i]->ncols > (1ull << 31)) return XFER_E_INVAL;
@@ -319,23 +330,48 @@ int xfer_argmax_merge(const xfer_shard *s0, const xfer_shard *s1, int mode, void
     if (rows > 1 && s[i]->ld < s[i]->ncols) return XFER_E_INVAL;
     uint64_t last_row;
     if (!mul_ok((uint64_t)(rows - 1), s[i]->ld, &last_row)) return XFER_E_INVAL;
-    lo[i] = (uintptr_t)s[i]->ptr;
-    span[i] = (last_row + s[i]->ncols) * 2;
+    c->lo[i] = (uintptr_t)s[i]->ptr;
+    c->span[i] = (last_row + s[i]->ncols) * 2;
   }
-  const uint32_t splits = xfer::argmax_splits(rows, s0->ncols, s1->ncols);
-  if ((uint64_t)rows * 2 * splits > xfer::kMaxGridBlocks) return XFER_E_UNSUPPORTED;
-  const uint64_t need = xfer::argmax_workspace_bytes(rows, splits);
+  c->splits = xfer::argmax_splits(rows, s0->ncols, s1->ncols);
+  if ((uint64_t)rows * 2 * c->splits > xfer::kMaxGridBlocks) return XFER_E_UNSUPPORTED;
+  c->need = xfer::argmax_workspace_bytes(rows, c->splits);
   if (!out || !aligned16(out)) return XFER_E_INVAL;
-  if (!workspace || !aligned16(workspace) || workspace_bytes < need) return XFER_E_INVAL;
   const uint64_t out_bytes = (uint64_t)rows * (mode == XFER_ARGMAX ? sizeof(xfer_max_idx) : sizeof(xfer_top2));
-  for (int i = 0; i < 2; ++i) {
-    if (overlaps((uintptr_t)out, out_bytes, lo[i], span[i])) return XFER_E_INVAL;
-    if (overlaps((uintptr_t)workspace, need, lo[i], span[i])) return XFER_E_INVAL;
-  }
-  if (overlaps((uintptr_t)out, out_bytes, (uintptr_t)workspace, need)) return XFER_E_INVAL;
-  xfer::ArgmaxShard a{s0->ptr, s0->ld, s0->ncols, s0->col_offset};
-  xfer::ArgmaxShard b{s1->ptr, s1->ld, s1->ncols, s1->col_offset};
-  if (xfer::launch_argmax(a, b, rows, mode, out, workspace, splits, stream) != hipSuccess) return XFER_E_DEVICE;
+  for (int i = 0; i < 2; ++i)
+    if (overlaps((uintptr_t)out, out_bytes, c->lo[i], c->span[i])) return XFER_E_INVAL;
+  c->a = xfer::ArgmaxShard{s0->ptr, s0->ld, s0->ncols, s0->col_offset};
+  c->b = xfer::ArgmaxShard{s1->ptr, s1->ld, s1->ncols, s1->col_offset};
+  return XFER_OK;
+}
+
+}  // namespace
+
+int xfer_argmax_merge(const xfer_shard *s0, const xfer_shard *s1, int mode, void *out, void *workspace,
+                      size_t workspace_bytes, hipStream_t stream) {
+  ArgmaxCall c;
+  const int st = argmax_checks(s0, s1, mode, out, &c);
+  if (st != XFER_OK || c.rows == 0) return st;
+  if (!workspace || !aligned16(workspace) || workspace_bytes < c.need) return XFER_E_INVAL;
+  const uint64_t out_bytes = (uint64_t)c.rows * (mode == XFER_ARGMAX ? sizeof(xfer_max_idx) : sizeof(xfer_top2));
+  for (int i = 0; i < 2; ++i)
+    if (overlaps((uintptr_t)workspace, c.need, c.lo[i], c.span[i])) return XFER_E_INVAL;
+  if (overlaps((uintptr_t)out, out_bytes, (uintptr_t)workspace, c.need)) return XFER_E_INVAL;
+  if (xfer::launch_argmax(c.a, c.b, c.rows, mode, out, workspace, c.splits, stream) != hipSuccess)
+    return XFER_E_DEVICE;
+  return XFER_OK;
+}
+
+int xfer_argmax_merge_noalloc(const xfer_shard *s0, const xfer_shard *s1, int mode, void *out,
+                              hipStream_t stream) {
+  ArgmaxCall c;
+  const int st = argmax_checks(s0, s1, mode, out, &c);
+  if (st != XFER_OK || c.rows == 0) return st;
+  if (c.need > xfer::kArgmaxScratchBytes) return XFER_E_UNSUPPORTED;
+  void *scratch = nullptr;
+  if (xfer::argmax_scratch(&scratch) != hipSuccess) return XFER_E_DEVICE;
+  if (xfer::launch_argmax(c.a, c.b, c.rows, mode, out, scratch, c.splits, stream) != hipSuccess)
+    return XFER_E_DEVICE;
   return XFER_OK;
 }
 

@@ -25,9 +25,46 @@
 // elements of any set follow from the pairwise merge
 //     top1 = max(x1, y1), top2 = max(min(x1, y1), max(x2, y2)).
 // The wavefront reductions use DPP lane moves.
+#include <atomic>
+#include <mutex>
+
 #include "internal.h"
 
 namespace xfer {
+
+// Partial records of xfer_argmax_merge_noalloc: a static device array in
+// place of the caller's workspace, one copy per GPU at its own address.  In
+// host code `scratch` names a host-side stand-in, never the device memory:
+// the device address comes from hipGetSymbolAddress, looked up once per
+// device with that device current, and only that address reaches a kernel.
+static __device__ __align__(256) uint64_t scratch[kArgmaxScratchBytes / sizeof(uint64_t)];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<void *> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+}  // namespace
+
+hipError_t argmax_scratch(void **ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void *p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return e;
+      if (!p) return hipErrorInvalidSymbol;
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *ptr = p;
+  return hipSuccess;
+}
+
 namespace {
 
 constexpr int kThreads = 256;

@@ -79,6 +79,11 @@ uint32_t argmax_splits(uint32_t rows, uint32_t ncols0, uint32_t ncols1);
 uint64_t argmax_workspace_bytes(uint32_t rows, uint32_t splits);
 hipError_t launch_argmax(ArgmaxShard s0, ArgmaxShard s1, uint32_t rows, int mode, void *out, void *workspace,
                          uint32_t splits, hipStream_t stream);
+// The library's own argmax partials array (xfer_argmax_merge_noalloc): its
+// device address on the current device, looked up on the first call made
+// with that device current and kept per device.
+constexpr uint64_t kArgmaxScratchBytes = XFER_ARGMAX_SCRATCH_BYTES;
+hipError_t argmax_scratch(void **ptr);
 
 // ---- run-table gather / scatter (runs_copy.hip)
 struct PlanView {

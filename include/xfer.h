@@ -206,6 +206,31 @@ XFER_API size_t xfer_argmax_workspace_bytes(uint32_t rows, uint32_t ncols0, uint
 XFER_API int xfer_argmax_merge(const xfer_shard *s0, const xfer_shard *s1, int mode, void *out, void *workspace,
                       size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * xfer_argmax_merge_noalloc - xfer_argmax_merge for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  It takes no workspace; the per-slice
+ * partial records go to a static device array of the library,
+ * XFER_ARGMAX_SCRATCH_BYTES bytes on each GPU the library runs on, held
+ * until the process ends.  The array's address on a device is looked up
+ * (hipGetSymbolAddress) on the first call made with that device current and
+ * kept; the call allocates nothing and needs no initialised memory (every
+ * partial record is written before it is read).
+ *
+ * Every call on one GPU shares that GPU's array and leaves its last
+ * contents there: calls that may overlap in time on one GPU (on different
+ * streams, or from different host threads without ordering) race, and their
+ * outputs are then undefined.  Order such calls on one stream.
+ *
+ * Arguments, outputs and errors as xfer_argmax_merge without the workspace,
+ * plus XFER_E_UNSUPPORTED when the partial records need more than
+ * XFER_ARGMAX_SCRATCH_BYTES (xfer_argmax_workspace_bytes above it: more than
+ * 4096 rows), and XFER_E_DEVICE if the array's address cannot be obtained.
+ */
+#define XFER_ARGMAX_SCRATCH_BYTES 65536
+XFER_API int xfer_argmax_merge_noalloc(const xfer_shard *s0, const xfer_shard *s1, int mode, void *out,
+                                       hipStream_t stream);
+
 /* ------------------------------------------------------------- run tables */
 
 /*

@@ -102,6 +102,37 @@ void argmax(Rng &g) {
     clash.col_offset = n0 - 1;  // overlaps shard 0's ids
     CHECK(xfer_argmax_merge(&s0, &clash, mode, out.p, ws.p, wsb, token(3)) == XFER_E_INVAL);
     CHECK(xfer_argmax_merge(&s0, &s1, mode, m.p, ws.p, wsb, token(3)) == XFER_E_INVAL);  // out over the logits
+    // the form with the library's static partials array: same checks, no workspace
+    CHECK(xfer_argmax_merge_noalloc(&s0, &s1, mode, out.p, token(3)) == XFER_OK);
+    CHECK(mock::g_last.a == rows);
+    CHECK(xfer_argmax_merge_noalloc(&s0, &clash, mode, out.p, token(3)) == XFER_E_INVAL);
+    CHECK(xfer_argmax_merge_noalloc(&s0, &s1, mode, m.p, token(3)) == XFER_E_INVAL);
+    CHECK(xfer_argmax_merge_noalloc(&s0, &s1, mode, nullptr, token(3)) == XFER_E_INVAL);
+    CHECK(xfer_argmax_merge_noalloc(&s0, &s1, 5, out.p, token(3)) == XFER_E_INVAL);
+  }
+  // partial records beyond the static array: refused before any launch
+  {
+    const uint32_t ld = 16;
+    for (uint32_t rows : {4096u, 4097u}) {
+      Buf m((size_t)rows * ld * 2), out((size_t)rows * 16);
+      xfer_shard s0{(const uint16_t *)m.p, ld, rows, 8, 0};
+      xfer_shard s1{(const uint16_t *)m.p + 8, ld, rows, 8, 8};
+      const bool fits = xfer_argmax_workspace_bytes(rows, 8, 8) <= XFER_ARGMAX_SCRATCH_BYTES;
+      const long before = mock::g_launches;
+      CHECK(xfer_argmax_merge_noalloc(&s0, &s1, XFER_TOP2, out.p, token(3)) ==
+            (fits ? XFER_OK : XFER_E_UNSUPPORTED));
+      CHECK(mock::g_launches == before + (fits ? 1 : 0));
+      CHECK(fits == (rows <= 4096));
+    }
+    Buf m(64), out(16);
+    xfer_shard s0{(const uint16_t *)m.p, 16, 1, 8, 0};
+    xfer_shard s1{(const uint16_t *)m.p + 8, 16, 1, 8, 8};
+    mock::fail_scratch(true);
+    CHECK(xfer_argmax_merge_noalloc(&s0, &s1, XFER_ARGMAX, out.p, token(3)) == XFER_E_DEVICE);
+    mock::reset_failures();
+    xfer_shard e0 = s0, e1 = s1;
+    e0.rows = e1.rows = 0;
+    CHECK(xfer_argmax_merge_noalloc(&e0, &e1, XFER_ARGMAX, nullptr, token(3)) == XFER_OK);  // empty work
   }
 }
 
@@ -418,6 +449,7 @@ void refused_launches() {
   CHECK(xfer_combine2_f32((const float *)src.p, (const float *)f1.p, n, out.p, XFER_OUT_BF16, token(1)) ==
         XFER_E_DEVICE);
   CHECK(xfer_argmax_merge(&s0, &s1, XFER_TOP2, rec.p, ws.p, ws.n, token(1)) == XFER_E_DEVICE);
+  CHECK(xfer_argmax_merge_noalloc(&s0, &s1, XFER_TOP2, rec.p, token(1)) == XFER_E_DEVICE);
   CHECK(xfer_gather_runs(&sp, stg.p, stg.n, token(1)) == XFER_E_DEVICE);
   CHECK(xfer_scatter_runs(stg.p, stg.n, &dp, token(1)) == XFER_E_DEVICE);
   CHECK(xfer_copy_descs(&fp, stg.p, stg.n, token(1)) == XFER_E_DEVICE);

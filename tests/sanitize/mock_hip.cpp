@@ -20,6 +20,7 @@ int g_fail_record_at = -1;
 int g_memcpy_calls = 0;
 int g_fail_memcpy_at = -1;
 bool g_fail_launches = false;
+bool g_fail_scratch = false;
 
 [[noreturn]] void die(const char *what) {
   std::fprintf(stderr, "mock hip: %s\n", what);
@@ -39,8 +40,10 @@ void reset_failures() {
   g_fail_create_at = g_fail_record_at = g_fail_memcpy_at = -1;
   g_create_calls = g_record_calls = g_memcpy_calls = 0;
   g_fail_launches = false;
+  g_fail_scratch = false;
 }
 void fail_launches(bool on) { g_fail_launches = on; }
+void fail_scratch(bool on) { g_fail_scratch = on; }
 void fail_event_create_at(int k) { g_create_calls = 0; g_fail_create_at = k; }
 void fail_event_record_at(int k) { g_record_calls = 0; g_fail_record_at = k; }
 void fail_memcpy_at(int k) { g_memcpy_calls = 0; g_fail_memcpy_at = k; }
@@ -158,6 +161,14 @@ hipError_t launch_argmax(ArgmaxShard s0, ArgmaxShard s1, uint32_t rows, int mode
   touch(out, (uint64_t)rows * (mode == XFER_ARGMAX ? 8 : 16));
   touch(workspace, argmax_workspace_bytes(rows, splits));
   return note("argmax", rows, (uint64_t)mode, splits);
+}
+
+// The library's static argmax array: host memory of the same size here.
+hipError_t argmax_scratch(void **ptr) {
+  alignas(256) static uint8_t buf[kArgmaxScratchBytes];
+  if (g_fail_scratch) return hipErrorInvalidValue;
+  *ptr = buf;
+  return hipSuccess;
 }
 
 hipError_t launch_gather(const PlanView &p, void *staging, hipStream_t) {

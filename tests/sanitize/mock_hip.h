@@ -16,4 +16,5 @@ void fail_event_record_at(int k);
 void fail_memcpy_at(int k);
 size_t live_events();
 void fail_launches(bool on);       // every launcher returns an error while on
+void fail_scratch(bool on);        // the static argmax array's lookup fails while on
 }  // namespace mock

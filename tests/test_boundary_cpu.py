@@ -26,7 +26,7 @@ def _declared():
 
 def test_library_exports_every_declared_call():
     names = _declared()
-    assert len(names) == 27
+    assert len(names) == 28
     assert set(names) == set(x.EXPORTED)
     L = x.lib()
     for n in names:
@@ -116,6 +116,30 @@ def test_argmax_argument_checks():
     assert f(s0, s1, out=0x100000 + 64) == x.E_INVAL              # out inside the logits
     assert f(s0, s1, ws=0x100000 + 64) == x.E_INVAL               # workspace inside the logits
     assert f(s0, s1, out=0xA00000 + 32) == x.E_INVAL              # out inside the workspace
+
+
+def test_argmax_noalloc_argument_checks():
+    """The no-allocation form runs the same checks, and refuses on the host
+    (before any runtime call) partial records that need more than the
+    library's static array: more than 4096 rows."""
+    f = lambda s0, s1, mode=0, out=0x900000: x.argmax_merge_noalloc_raw(s0, s1, mode, out, stream=S0)
+    s0 = _sh()
+    s1 = _sh(ptr=0x100000 + 1024, ncols=512, off=512)
+    assert f(s0, s1, mode=2) == x.E_INVAL
+    assert f(s0, _sh(rows=3, off=512, ptr=0x100400)) == x.E_INVAL
+    assert f(_sh(rows=0), _sh(rows=0, off=512), out=0) == x.OK    # no rows: empty work
+    assert f(s0, _sh(off=100, ptr=0x100400)) == x.E_INVAL
+    assert f(_sh(ncols=70000, ld=70000), _sh(off=70000, ptr=0x200000)) == x.E_UNSUPPORTED
+    assert f(s0, s1, out=0) == x.E_INVAL
+    assert f(s0, s1, out=0x900008) == x.E_INVAL                   # misaligned output
+    assert f(s0, s1, out=0x100000 + 64) == x.E_INVAL              # out inside the logits
+    ld = 64768 + 64512
+    big = 4097
+    assert x.argmax_workspace_bytes(4096, 64768, 64512) <= x.ARGMAX_SCRATCH_BYTES
+    assert x.argmax_workspace_bytes(big, 64768, 64512) > x.ARGMAX_SCRATCH_BYTES
+    b0 = x.shard(1 << 32, ld, big, 64768, 0)
+    b1 = x.shard((1 << 32) + 2 * 64768, ld, big, 64512, 64768)
+    assert f(b0, b1, out=1 << 40) == x.E_UNSUPPORTED              # beyond the static array
 
 
 def test_argmax_workspace_size_is_monotone_and_small():
