@@ -2,23 +2,31 @@
 """Benchmark of the transfer staging / combine hot path on one MI355X.
 
 One step is one pass of every hot-path kernel over one batch of synthetic,
-HBM-resident input:
-  pack_bf16 rank 0, pack_bf16 rank 1   2048 x 5120 F32 partials -> BF16, 512 KiB
+HBM-resident input.  The default workload ("fragmented") is the largest
+configuration that fits one GPU:
+  pack_bf16 rank 0, pack_bf16 rank 1   16384 x 5120 F32 partials -> BF16, 512 KiB
                                        chunks (bulk: every chunk in one call)
-  gather_runs                          1000 blocks x 288 slots x 2 x 4 KiB from two
-                                       bump-allocated regions -> dense staging
+  gather_runs (greedy table)           1000 blocks x 288 slots x 2 x 4 KiB from two
+                                       regions whose blocks sit in a seeded shuffled
+                                       order (288,000 runs) -> dense staging
+  gather_runs (one run per segment)    the same set by 576,000 runs -> a second staging
   scatter_runs                         staging -> destination, 12 KiB slot stride
   argmax_merge (top1, top2, idx)       16 rows x 129280 BF16 logits, 2 shards
   combine2 (F32 out)                   the two packed partials summed in F32
 combine runs last so its inputs, written by the packs, have been pushed out
-of the caches by the 9.4 GB the gather and scatter stream: every kernel
-reads from HBM, as in a cold pipeline.
+of the caches by the gathers and the scatter: every kernel reads from HBM,
+as in a cold pipeline.  `--workload step` is the smaller step (2048 x 5120
+partials, bump-allocated blocks: one run per lane).
 
 Prints ONE JSON line: value = algorithmic bytes of the whole step / wall
 time of the step (GB/s, decimal).  The roofline kernel's duration comes from
 HIP events recorded around it, on the stream it is launched on, in every
-timed step; the per-kernel breakdown ("kernels") comes from a separate,
-untimed pass with events around every kernel.
+timed step.  The per-kernel breakdown ("kernels") comes from a separate,
+untimed pass with events around every kernel; it also times kernels that are
+not in the step (the 2048 x 5120 pack and combine, and combine's BF16
+output mode).  After timing, every output of the last step and of the
+breakdown pass is compared byte for byte with the CPU oracle on the same
+inputs ("verified"); a mismatch makes the run exit with status 1.
 """
 import argparse
 import hashlib
@@ -32,6 +40,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0            # MI355X HBM3E, published
+METRIC = "achieved HBM GB/s (and % of peak) for pack+combine and run-table segment gather"
 CHUNK = 512 * 1024               # BF16 bytes per chunk
 TOKENS, HIDDEN = 2048, 5120
 ROWS, VOCAB, SPLIT = 16, 129280, 64768
@@ -97,7 +106,7 @@ class Workload:
     table, and a second table with one run per segment, are both gathered)."""
 
     def __init__(self, dev, tokens=TOKENS, shuffled=False, n_blocks=N_BLOCKS, seg=SEG, coalesced=False,
-                 streamed=False, f32wire=False, paged=False):
+                 streamed=False, f32wire=False, paged=False, extras=False):
         import numpy as np
         import torch
 
@@ -120,6 +129,25 @@ class Workload:
         self.ring_a = torch.zeros(self.n_chunks * CHUNK // 2, dtype=torch.int16, device=dev)
         self.ring_b = torch.zeros(self.n_chunks * CHUNK // 2, dtype=torch.int16, device=dev)
         self.sum = torch.zeros(n, dtype=torch.float32, device=dev)
+        # kernels timed in the breakdown pass only: combine's BF16 output mode,
+        # and the 2048 x 5120 pack and combine when the step's partials are larger
+        self.extras = extras
+        if extras:
+            self.sum_bf16 = torch.zeros(n, dtype=torch.int16, device=dev)
+            self.small = None
+            if tokens != TOKENS:
+                m = TOKENS * HIDDEN
+                self.small_a_host = dg.prompt_partial(m, _seed(dg, 2, 0, TOKENS))
+                self.small_b_host = dg.prompt_partial(m, _seed(dg, 2, 1, TOKENS))
+                nc = -(-m // (CHUNK // 2))
+                self.small = {
+                    "n": m, "n_chunks": nc,
+                    "a": torch.from_numpy(self.small_a_host).to(dev), "b": torch.from_numpy(self.small_b_host).to(dev),
+                    "ring_a": torch.zeros(nc * CHUNK // 2, dtype=torch.int16, device=dev),
+                    "ring_b": torch.zeros(nc * CHUNK // 2, dtype=torch.int16, device=dev),
+                    "sum": torch.zeros(m, dtype=torch.float32, device=dev),
+                    "sum_bf16": torch.zeros(m, dtype=torch.int16, device=dev),
+                }
 
         inp = dg.argmax_logits(ROWS, _seed(dg, 3))
         self.logits_host = inp.logits
@@ -152,6 +180,8 @@ class Workload:
             self.seg_plan_buf = torch.zeros(x.runs_plan_bytes(self.seg_table), dtype=torch.uint8, device=dev)
             self.seg_plan = x.runs_prepare(self.seg_table, [(b, rb) for b in bases], False, self.seg_plan_buf)
         self.staging = torch.empty(2 * N_SLOTS * B * SG, dtype=torch.uint8, device=dev)
+        # the per-segment gather writes its own staging, so both gathers are checked
+        self.staging_seg = torch.empty_like(self.staging) if shuffled else None
         self.fetch_plan = None
         if coalesced:
             # the whole source set read by dense-group descriptors into one slab
@@ -246,7 +276,7 @@ class Workload:
             ("gather", lambda: x.gather_runs(self.src_plan, self.staging)),
         ]
         if self.seg_plan is not None:
-            ks.append(("gather_per_segment", lambda: x.gather_runs(self.seg_plan, self.staging)))
+            ks.append(("gather_per_segment", lambda: x.gather_runs(self.seg_plan, self.staging_seg)))
         if self.fetch_plan is not None:
             ks.append(("fetch_coalesced", lambda: x.copy_descs(self.fetch_plan, self.slab)))
         ks += [
@@ -255,6 +285,60 @@ class Workload:
             ("combine_f32", lambda: x.combine2(ra[:n], rb[:n], self.sum, x.OUT_F32)),
         ]
         return ks
+
+    def extra_kernels(self):
+        """(name, callable) timed in the breakdown pass only, not in the step."""
+        if not self.extras:
+            return []
+        x, n = self.x, self.n
+        ks = [("combine_bf16", lambda: x.combine2(self.ring_a[:n], self.ring_b[:n], self.sum_bf16, x.OUT_BF16))]
+        sm = self.small
+        if sm is not None:
+            m, nc = sm["n"], sm["n_chunks"]
+            tag = f"{TOKENS}x{HIDDEN}"
+            ks = [
+                (f"pack_rank0_{tag}", lambda: x.pack_bf16(sm["a"], sm["ring_a"], CHUNK, 0, nc)),
+                (f"pack_rank1_{tag}", lambda: x.pack_bf16(sm["b"], sm["ring_b"], CHUNK, 0, nc)),
+                (f"combine_f32_{tag}", lambda: x.combine2(sm["ring_a"][:m], sm["ring_b"][:m], sm["sum"], x.OUT_F32)),
+                (f"combine_bf16_{tag}", lambda: x.combine2(sm["ring_a"][:m], sm["ring_b"][:m], sm["sum_bf16"],
+                                                           x.OUT_BF16)),
+            ] + ks
+        return ks
+
+    def step_outputs(self):
+        """Device buffers the step writes, by name (checked against the oracle)."""
+        if self.streamed:
+            return {"allreduce_rank0": self.outs[0], "allreduce_rank1": self.outs[1]}
+        if self.f32wire:
+            return {"combine_f32wire_20x5120": self.out_rows, "combine_f32wire_full": self.out_all}
+        if self.paged:
+            return {"paged_staging": self.staging, "paged_destination": self.dst}
+        outs = {"ring_rank0": self.ring_a, "ring_rank1": self.ring_b, "gather_staging": self.staging,
+                "scatter_destination": self.dst, "argmax_top2": self.top2, "combine_f32": self.sum}
+        if self.staging_seg is not None:
+            outs["gather_per_segment_staging"] = self.staging_seg
+        if self.fetch_plan is not None:
+            outs["fetch_slab"] = self.slab
+        return outs
+
+    def extra_outputs(self):
+        """Device buffers the breakdown-only kernels write, by name."""
+        if not self.extras:
+            return {}
+        outs = {"combine_bf16": self.sum_bf16}
+        sm = self.small
+        if sm is not None:
+            tag = f"{TOKENS}x{HIDDEN}"
+            outs.update({f"ring_rank0_{tag}": sm["ring_a"], f"ring_rank1_{tag}": sm["ring_b"],
+                         f"combine_f32_{tag}": sm["sum"], f"combine_bf16_{tag}": sm["sum_bf16"]})
+        return outs
+
+    def extra_bytes(self):
+        ab = {}
+        for name, _ in self.extra_kernels():
+            m = self.small["n"] if name.endswith(f"_{TOKENS}x{HIDDEN}") else self.n
+            ab[name] = (6 if name.startswith(("pack", "combine_bf16")) else 8) * m
+        return ab
 
     def algorithmic_bytes(self):
         if self.streamed:
@@ -281,19 +365,19 @@ def _events():
     return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
 
-def run_gpu(steps, warmup, workload):
+def run_gpu(w, steps, warmup, roofline_kernel, expected):
     """Warm up, then time `steps` whole steps (wall clock, synchronised on both
     sides).  Inside the timed region only the roofline kernel is bracketed by
     HIP events (on the stream it is launched on), so the step's wall time
-    carries one event pair per step, not one per kernel.  A separate, untimed
-    pass of up to 50 steps then brackets every kernel for the breakdown."""
+    carries one event pair per step, not one per kernel.  The outputs of the
+    last timed step are then compared with the oracle's (`expected`).  A
+    separate, untimed pass of up to 50 steps brackets every kernel for the
+    breakdown, followed by the breakdown-only kernels, whose outputs are
+    compared last."""
     import torch
 
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    w = Workload(dev, **WORKLOADS[workload]["args"])
     ks = w.kernels()
-    rk = WORKLOADS[workload]["roofline_kernel"][0]
+    rk = roofline_kernel
     log(f"bench: warmup {warmup} steps")
     for _ in range(warmup):
         for _, k in ks:
@@ -316,10 +400,13 @@ def run_gpu(steps, warmup, workload):
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     roofline_ms = sum(a.elapsed_time(b) for a, b in live) / len(live)
+    log("bench: checking the last timed step against the oracle")
+    checked = verify(w.step_outputs(), expected)
     log("bench: per-kernel breakdown pass")
-    events = {name: [] for name, _ in ks}
+    allk = ks + w.extra_kernels()
+    events = {name: [] for name, _ in allk}
     for _ in range(min(steps, 50)):
-        for name, k in ks:
+        for name, k in allk:
             e0, e1 = _events()
             e0.record()
             k()
@@ -327,7 +414,39 @@ def run_gpu(steps, warmup, workload):
             events[name].append((e0, e1))
     torch.cuda.synchronize()
     per_kernel_ms = {name: sum(a.elapsed_time(b) for a, b in ev) / len(ev) for name, ev in events.items()}
-    return w, elapsed, per_kernel_ms, roofline_ms
+    checked.update(verify(w.extra_outputs(), expected))
+    return elapsed, per_kernel_ms, roofline_ms, checked
+
+
+def verify(outputs, expected, chunk=1 << 28):
+    """Compare device buffers with the oracle's bytes, chunk by chunk.
+    Returns {name: bytes compared}; raises Mismatch naming the first
+    differing buffer and byte offset."""
+    import numpy as np
+
+    done = {}
+    for name, t in outputs.items():
+        want = expected[name].reshape(-1).view(np.uint8)
+        got_t = t.reshape(-1).view(torch_uint8())
+        if got_t.numel() != want.size:
+            raise Mismatch(f"{name}: device {got_t.numel()} bytes, oracle {want.size} bytes")
+        for off in range(0, want.size, chunk):
+            got = got_t[off:off + chunk].cpu().numpy()
+            ref = want[off:off + chunk]
+            if not np.array_equal(got, ref):
+                bad = off + int(np.flatnonzero(got != ref)[0])
+                raise Mismatch(f"{name}: first differing byte at offset {bad}")
+        done[name] = int(want.size)
+    return done
+
+
+class Mismatch(RuntimeError):
+    pass
+
+
+def torch_uint8():
+    import torch
+    return torch.uint8
 
 
 def isolated_cold(w, reps=20):
@@ -401,42 +520,110 @@ def isolated_cold(w, reps=20):
     return out
 
 
-def cpu_baseline(w, budget_s=12.0):
-    """The oracle, as it is, on this host: the same step (same sizes, same
-    inputs) repeated until about budget_s seconds of work; buffers are
-    allocated and touched before the clock starts."""
+def oracle_step(w, bufs=None):
+    """One step of the CPU oracle on the workload's host inputs, into `bufs`
+    (allocated on the first call): the expected bytes of every output the
+    step writes, by the names Workload.step_outputs uses."""
     import numpy as np
 
     import oracle
 
-    n = w.n
-    ce = CHUNK // 2
-    ring_a = np.ones(w.n_chunks * ce, np.uint16)
-    ring_b = np.ones(w.n_chunks * ce, np.uint16)
+    n, ce = w.n, CHUNK // 2
+    if bufs is None:
+        bufs = {"ring_rank0": np.zeros(w.n_chunks * ce, np.uint16), "ring_rank1": np.zeros(w.n_chunks * ce, np.uint16),
+                "gather_staging": np.zeros(2 * N_SLOTS * w.n_blocks * w.seg, np.uint8),
+                "scatter_destination": np.full(w.dst.numel(), 0xA5, np.uint8)}
+        if w.seg_plan is not None:
+            bufs["gather_per_segment_staging"] = np.zeros_like(bufs["gather_staging"])
     regions = [(r.data_ptr(), h) for r, h in zip(w.regions, w.region_hosts)]
-    src_t = oracle.RunTable(w.src_table.runs_per_lane, w.src_table.run_base, w.src_table.run_stride,
-                            w.src_table.run_count, w.n_blocks)
-    dst_t = oracle.RunTable(w.dst_table.runs_per_lane, w.dst_table.run_base, w.dst_table.run_stride,
-                            w.dst_table.run_count, w.n_blocks)
-    staging = np.ones(2 * N_SLOTS * w.n_blocks * w.seg, np.uint8)
-    dst = np.full(w.dst.numel(), 0xA5, np.uint8)
-    dst_regions = [(w.dst.data_ptr(), dst)]
-    step_bytes = sum(w.algorithmic_bytes().values())
-    seg_t = None
+    oracle.pack(w.a_host, w.n_chunks * ce, ce, 0, w.n_chunks, ring=bufs["ring_rank0"])
+    oracle.pack(w.b_host, w.n_chunks * ce, ce, 0, w.n_chunks, ring=bufs["ring_rank1"])
+    oracle.gather(_oracle_table(w.src_table, w.n_blocks), w.seg, regions, staging=bufs["gather_staging"])
     if w.seg_plan is not None:
-        seg_t = oracle.RunTable(w.seg_table.runs_per_lane, w.seg_table.run_base, w.seg_table.run_stride,
-                                w.seg_table.run_count, w.n_blocks)
+        oracle.gather(_oracle_table(w.seg_table, w.n_blocks), w.seg, regions,
+                      staging=bufs["gather_per_segment_staging"])
+    oracle.scatter(_oracle_table(w.dst_table, w.n_blocks), w.seg, [(w.dst.data_ptr(), bufs["scatter_destination"])],
+                   bufs["gather_staging"])
+    bufs["argmax_top2"] = oracle.argmax_merge(w.logits_host, SPLIT, 1)
+    bufs["combine_f32"] = oracle.combine2(bufs["ring_rank0"][:n], bufs["ring_rank1"][:n], 0)
+    if w.fetch_plan is not None:
+        descs, _, _ = oracle.groups_plan(_oracle_table(w.src_table, w.n_blocks), w.seg,
+                                         [(r.data_ptr(), r.numel()) for r in w.regions])
+        slab = np.zeros(w.slab.numel(), np.uint8)
+        oracle.copy_descs(descs, regions, slab)
+        bufs["fetch_slab"] = slab
+    return bufs
+
+
+def _oracle_table(t, n_blocks):
+    import oracle
+    return oracle.RunTable(t.runs_per_lane, t.run_base, t.run_stride, t.run_count, n_blocks)
+
+
+def oracle_expected(w):
+    """The oracle's bytes for every output the workload's kernels write
+    (step and breakdown-only kernels), computed once, untimed."""
+    import numpy as np
+
+    import oracle
+
+    if w.streamed:
+        ce = CHUNK // 2
+        nc = -(-w.n // ce)
+        pa = oracle.pack(w.a_host, nc * ce, ce, 0, nc)[:w.n]
+        pb = oracle.pack(w.b_host, nc * ce, ce, 0, nc)[:w.n]
+        s = oracle.combine2(pa, pb, 0)
+        return {"allreduce_rank0": s, "allreduce_rank1": s}
+    if w.f32wire:
+        m = w.wire_rows * HIDDEN
+        return {"combine_f32wire_20x5120": oracle.combine2_f32(w.a_host[:m], w.b_host[:m], 1),
+                "combine_f32wire_full": oracle.combine2_f32(w.a_host, w.b_host, 1)}
+    if w.paged:
+        staging = np.zeros(w.staging.numel(), np.uint8)
+        for r in range(2):
+            si, di = w.page_idx[r]
+            oracle.paged_copy(w.seg, w.region_hosts[r], si, w.seg, 0, staging, di, w.seg, 0)
+        dst = np.full(w.dst.numel(), 0xA5, np.uint8)
+        si, di = w.page_idx[2]
+        oracle.paged_copy(w.seg, staging, si, w.seg, 0, dst, di, w.seg, 0)
+        return {"paged_staging": staging, "paged_destination": dst}
+    return oracle_step(w)
+
+
+def extra_expected(w, expected):
+    """The oracle's bytes for the breakdown-only kernels; the step's packed
+    partials are taken from `expected` (the oracle's step)."""
+    import oracle
+
+    out = {}
+    if not w.extras:
+        return out
+    ce = CHUNK // 2
+    pa, pb = expected["ring_rank0"][:w.n], expected["ring_rank1"][:w.n]
+    out["combine_bf16"] = oracle.combine2(pa, pb, 1)
+    sm = w.small
+    if sm is not None:
+        m, nc = sm["n"], sm["n_chunks"]
+        tag = f"{TOKENS}x{HIDDEN}"
+        ra = oracle.pack(w.small_a_host, nc * ce, ce, 0, nc)
+        rb = oracle.pack(w.small_b_host, nc * ce, ce, 0, nc)
+        out[f"ring_rank0_{tag}"], out[f"ring_rank1_{tag}"] = ra, rb
+        out[f"combine_f32_{tag}"] = oracle.combine2(ra[:m], rb[:m], 0)
+        out[f"combine_bf16_{tag}"] = oracle.combine2(ra[:m], rb[:m], 1)
+    return out
+
+
+def cpu_baseline(w, budget_s=12.0):
+    """The oracle, as it is, on this host: the same step (same sizes, same
+    inputs) repeated until about budget_s seconds of work (at least 3
+    steps); buffers are allocated and touched before the clock starts.
+    Returns the baseline record and the last step's outputs."""
+    step_bytes = sum(w.algorithmic_bytes().values())
+    bufs = oracle_step(w)
     reps, t_total, per_step = 0, 0.0, []
-    while t_total < budget_s and reps < 50:
+    while (t_total < budget_s or reps < 3) and reps < 50:
         t0 = time.perf_counter()
-        oracle.pack(w.a_host, ring_a.size, ce, 0, w.n_chunks, ring=ring_a)
-        oracle.pack(w.b_host, ring_b.size, ce, 0, w.n_chunks, ring=ring_b)
-        oracle.gather(src_t, w.seg, regions, staging=staging)
-        if seg_t is not None:
-            oracle.gather(seg_t, w.seg, regions, staging=staging)
-        oracle.scatter(dst_t, w.seg, dst_regions, staging)
-        oracle.argmax_merge(w.logits_host, SPLIT, 1)
-        oracle.combine2(ring_a[:n], ring_b[:n], 0)
+        oracle_step(w, bufs)
         per_step.append(time.perf_counter() - t0)
         t_total += per_step[-1]
         reps += 1
@@ -449,7 +636,7 @@ def cpu_baseline(w, budget_s=12.0):
         "sample": f"{reps} full steps of the same workload (same sizes and inputs), single-threaded C oracle, "
                   f"{t_total:.1f} s in all, median step {med * 1e3:.1f} ms (value from the median); host: "
                   f"{_cpu_model()}, {os.cpu_count()} logical CPUs",
-    }
+    }, bufs
 
 
 # hipDeviceAttribute_t values (ROCm 7.x hip_runtime_api.h): peak core clock,
@@ -498,17 +685,21 @@ def _cpu_model():
 
 WORKLOADS = {
     "step": {
-        "args": {"tokens": TOKENS, "shuffled": False},
+        "args": {"tokens": TOKENS, "shuffled": False, "extras": True},
+        "cpu_baseline": True,
         "describe": "transfer hot path: pack x2 + combine2 (2048x5120 F32 partials, 512 KiB BF16 chunks), "
                     "argmax merge (16x129280 BF16, split at 64768, top2), gather+scatter by run table "
                     "(1000 blocks x 288 slots x 2 x 4 KiB, one run per lane)",
         "roofline_kernel": ("gather", "gather_runs (paged K/V, 576 runs)", "runs_copy.hip", "gather_dense"),
     },
     "fragmented": {
-        "args": {"tokens": 16384, "shuffled": True},
-        "describe": "fragmented transfer: pack x2 + combine2 (16384x5120 F32 partials), argmax merge "
-                    "(16x129280), gather of 1000 x 288 x 2 x 4 KiB with a shuffled block order by the greedy "
-                    "run table (288,000 runs) and by one run per segment (576,000 runs), scatter",
+        "args": {"tokens": 16384, "shuffled": True, "extras": True},
+        "cpu_baseline": True,
+        "describe": "fragmented transfer (the largest single-GPU configuration): pack x2 + combine2 (16384x5120 F32 "
+                    "partials, 512 KiB BF16 chunks), argmax merge (16x129280 BF16, split at 64768, top2), gather of "
+                    "1000 blocks x 288 slots x 2 x 4 KiB whose blocks sit in a seeded shuffled order, by the greedy "
+                    "run table (288,000 runs) and by one run per segment (576,000 runs), scatter into a 12 KiB "
+                    "slot-stride destination",
         "roofline_kernel": ("gather", "gather_runs (shuffled blocks, 288,000 runs)", "runs_copy.hip",
                             "gather_fragmented"),
     },
@@ -572,8 +763,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", choices=sorted(WORKLOADS), default="step",
-                    help="step (default): the bench line; fragmented: the shuffled-layout / large-combine shapes")
+    ap.add_argument("--workload", choices=sorted(WORKLOADS), default="fragmented",
+                    help="fragmented (default): the largest single-GPU configuration; step: the 2048 x 5120 / "
+                         "bump-allocated step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy", action="store_true", help="run only the copy used to scale PMC readings")
     ap.add_argument("--isolated", action="store_true",
@@ -600,23 +792,53 @@ def main():
         sys.exit("--steps must be >= 1")
 
     wl = WORKLOADS[args.workload]
-    w, elapsed, kms, roofline_ms = run_gpu(args.steps, args.warmup, args.workload)
+    import torch
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = Workload(dev, **wl["args"])
+    baseline = None
+    if not args.no_cpu_baseline and wl.get("cpu_baseline"):
+        log("bench: cpu baseline (oracle); its last step is the expected output")
+        baseline, expected = cpu_baseline(w)
+    else:
+        log("bench: oracle outputs (untimed)")
+        expected = oracle_expected(w)
+    expected.update(extra_expected(w, expected))
+    rk, rk_label, rk_file, rk_key = wl["roofline_kernel"]
+    verified, verify_error, checked = True, None, {}
+    try:
+        elapsed, kms, roofline_ms, checked = run_gpu(w, args.steps, args.warmup, rk, expected)
+    except Mismatch as e:
+        verified, verify_error = False, str(e)
+        log(f"bench: OUTPUT MISMATCH against the oracle: {e}")
+    if not verified:
+        print(json.dumps({"metric": METRIC, "value": None, "verified": False, "verify_error": verify_error,
+                          "config": {"workload": wl["describe"]}}), flush=True)
+        sys.exit(1)
     ab = w.algorithmic_bytes()
     step_bytes = sum(ab.values())
+    ab_all = dict(ab, **w.extra_bytes())
     ms_per_step = elapsed / args.steps * 1e3
     value = step_bytes * args.steps / elapsed / 1e9
     kernels = {}
     for name, ms in kms.items():
-        gbs = ab[name] / (ms * 1e-3) / 1e9
-        kernels[name] = {"us": round(ms * 1e3, 2), "bytes": ab[name], "GBps": round(gbs, 1),
-                         "frac_of_peak": round(gbs / PEAK_HBM_GBS, 4)}
-    rk, rk_label, rk_file, rk_key = wl["roofline_kernel"]
+        gbs = ab_all[name] / (ms * 1e-3) / 1e9
+        kernels[name] = {"us": round(ms * 1e3, 2), "bytes": ab_all[name], "GBps": round(gbs, 1),
+                         "frac_of_peak": round(gbs / PEAK_HBM_GBS, 4), "in_step": name in ab}
+
+    def pack_combine(names):
+        if not all(n in kms for n in names):
+            return None
+        return round(sum(ab_all[n] for n in names) / (sum(kms[n] for n in names) * 1e-3) / 1e9, 1)
+
+    tag = f"{TOKENS}x{HIDDEN}"
     g_gbs = ab[rk] / (roofline_ms * 1e-3) / 1e9
     roofline = {"kernel": rk_label, "bound": "hbm", "achieved": round(g_gbs, 1),
                 "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(g_gbs / PEAK_HBM_GBS, 4),
                 "traffic": measured_traffic(rk_file, rk_key) if rk_file else None}
     line = {
-        "metric": "achieved HBM GB/s (and % of peak) for pack+combine and run-table segment gather",
+        "metric": METRIC,
         "value": round(value, 1),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -639,18 +861,18 @@ def main():
         },
         "device": device_info(),
         "kernels": kernels,
-        "pack_combine_GBps": (round((ab["pack_rank0"] + ab["pack_rank1"] + ab["combine_f32"]) /
-                                    ((kms["pack_rank0"] + kms["pack_rank1"] + kms["combine_f32"]) * 1e-3) / 1e9, 1)
-                              if "pack_rank0" in ab else None),
+        "pack_combine_GBps": pack_combine(("pack_rank0", "pack_rank1", "combine_f32")),
+        f"pack_combine_{tag}_GBps": (pack_combine((f"pack_rank0_{tag}", f"pack_rank1_{tag}", f"combine_f32_{tag}"))
+                                     or (pack_combine(("pack_rank0", "pack_rank1", "combine_f32"))
+                                         if w.tokens == TOKENS else None)),
         "roofline": roofline,
-        "cpu_baseline": None,
+        "verified": verified,
+        "verified_outputs": checked,
+        "cpu_baseline": baseline,
     }
     if args.isolated:
         log("bench: isolated cold pass")
         line["isolated_cold"] = isolated_cold(w)
-    if not args.no_cpu_baseline and args.workload == "step":
-        log("bench: cpu baseline (oracle)")
-        line["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(line), flush=True)
 
 
