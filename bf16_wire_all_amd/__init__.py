@@ -62,7 +62,7 @@ class AllReduce2Desc(ctypes.Structure):
     _fields_ = [("src", ctypes.c_void_p * 2), ("send", ctypes.c_void_p * 2), ("recv", ctypes.c_void_p * 2),
                 ("out", ctypes.c_void_p * 2), ("n", ctypes.c_size_t), ("chunk_bytes", ctypes.c_size_t),
                 ("ring_bytes", ctypes.c_size_t), ("out_mode", ctypes.c_int), ("compute", ctypes.c_void_p * 2),
-                ("wire", ctypes.c_void_p * 2), ("events", ctypes.c_void_p)]
+                ("wire", ctypes.c_void_p * 2), ("events", ctypes.c_void_p), ("n_events", ctypes.c_size_t)]
 
 
 class DescsPlan(ctypes.Structure):
@@ -445,6 +445,7 @@ def _allreduce2_desc(src, send, recv, out, chunk_bytes: int, mode: int, compute=
     d.ring_bytes = send[0].numel() * send[0].element_size() if ring_bytes is None else ring_bytes
     d.out_mode = mode
     d.events = ctypes.cast(events.array, ctypes.c_void_p) if events is not None else None
+    d.n_events = events.n if events is not None else 0
     return d
 
 

@@ -83,8 +83,9 @@ Layout layout_for(const xfer_run_table *t) {
   L.pieces = 1;
   if (t->seg_bytes > lane_bytes && (vps & (vps - 1)) == 0) L.pieces = (uint32_t)(t->seg_bytes / lane_bytes);
   L.group_blocks = kDefaultGroupBlocks;
-  L.n_tiles = (t->n_blocks + L.tile_blocks - 1) / L.tile_blocks;
-  L.n_groups = (t->n_blocks + L.group_blocks - 1) / L.group_blocks;
+  // Rounded up in 64 bits: n_blocks may be as large as 2^32 - 1.
+  L.n_tiles = (uint32_t)(((uint64_t)t->n_blocks + L.tile_blocks - 1) / L.tile_blocks);
+  L.n_groups = (uint32_t)(((uint64_t)t->n_blocks + L.group_blocks - 1) / L.group_blocks);
   L.off_group_run = 0;
   L.off_run_start = up16((uint64_t)t->n_lanes * (L.n_groups + 1) * 4);
   L.off_run_base = L.off_run_start + up16(t->n_runs * 4);
@@ -239,7 +240,8 @@ int xfer_pack_bf16(const float *src, size_t n, uint16_t *ring, size_t ring_bytes
   if (chunk_begin > chunk_end) return XFER_E_INVAL;
   const uint64_t R = ring_bytes / chunk_bytes;
   if (chunk_end - chunk_begin > R) return XFER_E_INVAL;
-  if (n == 0 || chunk_begin == chunk_end) return XFER_OK;
+  if (chunk_begin == chunk_end) return XFER_OK;
+  // n == 0 with a named chunk falls through: that chunk starts at or past n.
   if (!src || !ring || !aligned16(src) || !aligned16(ring)) return XFER_E_INVAL;
   const uint64_t ce = chunk_bytes / 2;
   const uint64_t n_chunks = n / ce + (n % ce != 0);

@@ -225,7 +225,8 @@ int xfer_allreduce2_streamed(const xfer_allreduce2_desc *d) {
   Call c;
   const int st0 = check_desc(d, &c);
   if (st0 != XFER_OK || c.n_chunks == 0) return st0;
-  if (!d->events) return XFER_E_INVAL;
+  // The schedule names event ids up to 6 * R - 1.
+  if (!d->events || d->n_events < 6 * c.R) return XFER_E_INVAL;
   hipStream_t streams[kStreams] = {d->compute[0], d->compute[1], d->wire[0], d->wire[1]};
   hipError_t err = hipSuccess;
   for_each_op((uint32_t)c.n_chunks, (uint32_t)c.R, [&](const xfer_op &op) {

@@ -31,7 +31,8 @@
  *     the HIP runtime refused; work enqueued before it may still run.  The
  *     outputs of a failed call must not be read.
  *   - Empty work (n == 0, rows == 0, an empty chunk range, an empty table) is
- *     XFER_OK with nothing enqueued.
+ *     XFER_OK with nothing enqueued; for xfer_pack_bf16 the chunk range is
+ *     what counts (a chunk named with n == 0 starts at n, XFER_E_INVAL).
  *   - Every buffer a kernel streams through, and every row start and segment
  *     address, must be 16-byte aligned: the kernels move 128-bit vectors.
  *     Element counts may be anything.
@@ -582,7 +583,8 @@ typedef struct {
   int out_mode;           /* XFER_OUT_F32 or XFER_OUT_BF16                            */
   hipStream_t compute[2]; /* rank r's conversion and sum stream                       */
   hipStream_t wire[2];    /* rank r's outgoing copy stream                            */
-  hipEvent_t *events;     /* 6 * R events from xfer_events_create                     */
+  hipEvent_t *events;     /* (host) n_events events from xfer_events_create           */
+  size_t n_events;        /* entries of events; at least 6 * R                        */
 } xfer_allreduce2_desc;
 
 /*
@@ -593,9 +595,10 @@ typedef struct {
  * this call.  A later call with the same rings and events is ordered after
  * this one by the events themselves.
  * Errors: XFER_E_INVAL for NULL or misaligned buffers, a bad chunk or ring
- * size, an unknown out_mode, any two of the ten buffers overlapping, or
- * fewer than 6 * R events; XFER_E_DEVICE if the runtime refuses an enqueue
- * (earlier chunks may already be enqueued).
+ * size, an unknown out_mode, any two of the eight buffers overlapping (the
+ * two sources excepted: both are only read), events NULL or n_events below
+ * 6 * R; XFER_E_DEVICE if the runtime refuses an enqueue (earlier chunks may
+ * already be enqueued).
  */
 XFER_API int xfer_allreduce2_streamed(const xfer_allreduce2_desc *d);
 

@@ -375,6 +375,9 @@ void streamed(Rng &g) {
     d.wire[0] = token(13);
     d.wire[1] = token(14);
     d.events = ev.data();
+    d.n_events = ev.size() - 1;
+    CHECK(xfer_allreduce2_streamed(&d) == (n ? XFER_E_INVAL : XFER_OK));  // one event short
+    d.n_events = ev.size();
     CHECK(xfer_allreduce2_streamed(&d) == XFER_OK);
     CHECK(xfer_allreduce2_streamed(&d) == XFER_OK);  // a second call on the same rings and events
     hipGraphExec_t ex = reinterpret_cast<hipGraphExec_t>((uintptr_t)1);
@@ -443,6 +446,7 @@ void refused_launches() {
   d.wire[0] = token(23);
   d.wire[1] = token(24);
   d.events = ev.data();
+  d.n_events = 12;
   mock::fail_launches(true);
   CHECK(xfer_pack_bf16((const float *)src.p, n, (uint16_t *)ring.p, 128, 64, 0, 2, token(1)) == XFER_E_DEVICE);
   CHECK(xfer_combine2((const uint16_t *)a.p, (const uint16_t *)b.p, n, out.p, XFER_OUT_F32, token(1)) == XFER_E_DEVICE);

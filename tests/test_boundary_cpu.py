@@ -50,7 +50,9 @@ def test_pack_argument_checks():
     assert f(src, 100, ring, 0, 32, 0, 1) == x.E_INVAL            # empty ring
     assert f(src, 100, ring, 64, 32, 2, 1) == x.E_INVAL           # begin > end
     assert f(src, 100, ring, 64, 32, 0, 3) == x.E_INVAL           # 3 chunks into 2 slots
-    assert f(src, 0, ring, 64, 32, 0, 1) == x.OK                  # n == 0: empty work
+    assert f(src, 0, ring, 64, 32, 0, 1) == x.E_INVAL             # n == 0: chunk 0 starts at n
+    assert f(src, 0, ring, 64, 32, 0, 0) == x.OK                  # n == 0, no chunk: empty work
+    assert f(0, 0, 0, 64, 32, 1, 1) == x.OK                       # empty range: nothing is read
     assert f(src, 100, ring, 64, 32, 1, 1) == x.OK                # empty chunk range
     assert f(0, 100, ring, 64, 32, 0, 1) == x.E_INVAL             # NULL src
     assert f(src + 4, 100, ring, 64, 32, 0, 1) == x.E_INVAL       # misaligned src

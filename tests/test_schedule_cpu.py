@@ -127,7 +127,7 @@ def test_streamed_argument_checks():
         d.recv[r] = base + 0x500000 + r * 0x10000
         d.out[r] = base + 0x600000 + r * 0x100000
     d.n, d.chunk_bytes, d.ring_bytes, d.out_mode = 1000, 64, 128, 0
-    d.events = 0x1234
+    d.events, d.n_events = 0x1234, 12
     L = x.lib()
     import ctypes
     for field, value in (("out_mode", 5), ("chunk_bytes", 24), ("ring_bytes", 96)):
@@ -140,6 +140,12 @@ def test_streamed_argument_checks():
     bad = x.AllReduce2Desc.from_buffer_copy(d)
     bad.out[0] = base + 8                     # misaligned and overlapping
     assert L.xfer_allreduce2_streamed(ctypes.byref(bad)) == x.E_INVAL
+    short = x.AllReduce2Desc.from_buffer_copy(d)
+    short.n_events = 11                        # two slots name event ids 0..11
+    assert L.xfer_allreduce2_streamed(ctypes.byref(short)) == x.E_INVAL
+    three = x.AllReduce2Desc.from_buffer_copy(d)
+    three.ring_bytes = 192                     # three slots need 18 events, not 12
+    assert L.xfer_allreduce2_streamed(ctypes.byref(three)) == x.E_INVAL
     empty = x.AllReduce2Desc.from_buffer_copy(d)
     empty.n = 0
     assert L.xfer_allreduce2_streamed(ctypes.byref(empty)) == x.OK
