@@ -34,8 +34,8 @@
  *     XFER_OK with nothing enqueued; for xfer_pack_bf16 the chunk range is
  *     what counts (a chunk named with n == 0 starts at n, XFER_E_INVAL).
  *   - Every buffer a kernel streams through, and every row start and segment
- *     address, must be 16-byte aligned: the kernels move 128-bit vectors.
- *     Element counts may be anything.
+ *     address, must be 16-byte aligned: the kernels move 64- and 128-bit
+ *     vectors.  Element counts may be anything.
  *   - Results are deterministic and independent of launch shape: the same
  *     inputs give the same bits on every call and on every GPU.
  */
