@@ -290,7 +290,7 @@ void runs_and_groups(Rng &g) {
 void pages(Rng &g) {
   for (int it = 0; it < 300; ++it) {
     const uint64_t page_len = 16 * (1 + g.below(it % 5 == 0 ? 1400 : 300));
-    const uint64_t n = g.below(200);
+    const uint64_t n = g.below(it % 7 == 0 ? 3000 : 200);  // some lists span several groups of 128 workgroups
     const uint64_t stride = page_len + 16 * g.below(4);
     const uint64_t slots = n + g.below(16) + 1;
     Buf src(slots * stride + 64), dst(slots * stride + 64);
@@ -304,7 +304,8 @@ void pages(Rng &g) {
     }
     const int trouble = (int)g.below(5);  // 0: none, 1: dst repeat, 2: page out of range, 3: huge stride
     if (trouble == 1 && n > 1) di[1] = di[0];
-    if (trouble == 2 && n) si[n - 1] = (uint32_t)slots;
+    if (trouble == 2 && n) si[n - 1] = (uint32_t)slots + 8;  // past the 64 bytes of slack for any stride
+    if (trouble == 3 && n) si[0] = 1;  // index 1 at a 2^62 stride lies outside the region
     const uint64_t sstride = trouble == 3 ? (1ull << 62) : stride;
     const xfer_region sr{src.addr(), src.n}, dr{dst.addr(), dst.n};
     const xfer_pages sp{si.data(), sstride, 16 * g.below(2)}, dp{di.data(), stride, 0};
