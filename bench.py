@@ -106,7 +106,7 @@ class Workload:
     table, and a second table with one run per segment, are both gathered)."""
 
     def __init__(self, dev, tokens=TOKENS, shuffled=False, n_blocks=N_BLOCKS, seg=SEG, coalesced=False,
-                 streamed=False, f32wire=False, paged=False, extras=False):
+                 streamed=False, f32wire=False, paged=False, extras=False, graph=False):
         import numpy as np
         import torch
 
@@ -240,6 +240,10 @@ class Workload:
             self.compute = [torch.cuda.Stream(device=dev) for _ in range(2)]
             self.wire = [torch.cuda.Stream(device=dev) for _ in range(2)]
             self.events = x.Events(6 * SLOTS)
+        # graph: the same schedule built once as a HIP graph over these buffers,
+        # launched on the current stream each step
+        self.graph = x.AllReduce2Graph((self.a, self.b), self.send, self.recv, self.outs, STREAM_CHUNK,
+                                       x.OUT_F32) if streamed and graph else None
         torch.cuda.synchronize()
 
     def _allreduce(self):
@@ -259,6 +263,8 @@ class Workload:
         x = self.x
         n, nc = self.n, self.n_chunks
         ra, rb = self.ring_a, self.ring_b
+        if self.graph is not None:
+            return [("allreduce2_graph", self.graph.launch)]
         if self.streamed:
             return [("allreduce2_streamed", self._allreduce)]
         if self.paged:
@@ -343,7 +349,7 @@ class Workload:
     def algorithmic_bytes(self):
         if self.streamed:
             # per rank: pack 6 B, wire copy 2 B read + 2 B written, combine F32 8 B per element
-            return {"allreduce2_streamed": 2 * 18 * self.n}
+            return {"allreduce2_graph" if self.graph is not None else "allreduce2_streamed": 2 * 18 * self.n}
         if self.paged:
             kv = self.n_blocks * N_SLOTS * 2 * self.seg
             return {"paged_gather_region0": kv, "paged_gather_region1": kv, "paged_scatter": 2 * kv}
@@ -741,6 +747,14 @@ WORKLOADS = {
         "roofline_kernel": ("allreduce2_streamed", "allreduce2_streamed (40 chunks x 2 ranks x pack/copy/combine)",
                             None, None),
     },
+    "streamed_graph": {
+        "args": {"tokens": TOKENS, "shuffled": False, "streamed": True, "graph": True},
+        "describe": "the streamed workload's all-reduce built once as a HIP graph (one kernel node per pack and "
+                    "combine, one copy node per wire copy, the streams' orderings as explicit dependencies) and "
+                    "launched on one stream each step",
+        "roofline_kernel": ("allreduce2_graph", "allreduce2 graph (40 chunks x 2 ranks x pack/copy/combine)",
+                            None, None),
+    },
 }
 
 
@@ -857,7 +871,7 @@ def main():
             "wire_dtype": "bf16",
             "inputs": "seeded synthetic: xoshiro256** seeded by SplitMix64, seed 0x5EED0000 + config "
                       f"+ (rank << 8) + (label << 16) + {SEED_OFFSET}",
-            **({"slots": SLOTS, "chunk_bytes": STREAM_CHUNK} if args.workload == "streamed" else {}),
+            **({"slots": SLOTS, "chunk_bytes": STREAM_CHUNK} if args.workload.startswith("streamed") else {}),
         },
         "device": device_info(),
         "kernels": kernels,

@@ -31,7 +31,7 @@ EXPORTED = [
     "xfer_groups_plan", "xfer_descs_plan_bytes", "xfer_descs_prepare", "xfer_copy_descs",
     "xfer_pages_plan_bytes", "xfer_pages_prepare", "xfer_paged_copy",
     "xfer_allreduce2_graph_create", "xfer_allreduce2_graph_launch", "xfer_allreduce2_graph_destroy",
-    "xfer_argmax_merge_noalloc",
+    "xfer_argmax_merge_noalloc", "xfer_allreduce2_graph_deps",
 ]
 
 
@@ -161,6 +161,8 @@ def lib():
         L.xfer_allreduce2_graph_launch.restype = I
         L.xfer_allreduce2_graph_destroy.argtypes = [P]
         L.xfer_allreduce2_graph_destroy.restype = I
+        L.xfer_allreduce2_graph_deps.argtypes = [U32, U32, P, P, S, ctypes.POINTER(S)]
+        L.xfer_allreduce2_graph_deps.restype = I
         L.xfer_pages_plan_bytes.argtypes = [U64]
         L.xfer_pages_plan_bytes.restype = S
         L.xfer_pages_prepare.argtypes = [U64, ctypes.POINTER(Region), ctypes.POINTER(PagesC), ctypes.POINTER(Region),
@@ -458,8 +460,8 @@ def allreduce2_streamed(src, send, recv, out, chunk_bytes: int, mode: int, compu
 
 
 class AllReduce2Graph:
-    """The streamed schedule recorded once as a HIP graph over fixed buffers
-    (src, send, recv, out as in allreduce2_streamed)."""
+    """The streamed schedule built once as a HIP graph over fixed buffers
+    (src, send, recv, out as in allreduce2_streamed; no streams or events)."""
 
     def __init__(self, src, send, recv, out, chunk_bytes: int, mode: int, ring_bytes: int | None = None):
         self._keep = (src, send, recv, out)       # the graph holds their addresses
@@ -481,6 +483,19 @@ class AllReduce2Graph:
             self.close()
         except Exception:
             pass
+
+
+def allreduce2_graph_deps(n_chunks: int, R: int):
+    """The graph form's dependencies as a list of (from, to) operation indices."""
+    n = ctypes.c_size_t(0)
+    st = lib().xfer_allreduce2_graph_deps(n_chunks, R, None, None, 0, ctypes.byref(n))
+    if st not in (OK, E_RANGE):
+        _check(st, "xfer_allreduce2_graph_deps")
+    frm = (ctypes.c_uint32 * max(1, n.value))()
+    to = (ctypes.c_uint32 * max(1, n.value))()
+    _check(lib().xfer_allreduce2_graph_deps(n_chunks, R, frm, to, n.value, ctypes.byref(n)),
+           "xfer_allreduce2_graph_deps")
+    return [(frm[k], to[k]) for k in range(n.value)]
 
 
 def allreduce2_graph_create_status(d: AllReduce2Desc) -> int:

@@ -24,6 +24,24 @@ static inline hipError_t launch(void (*kernel)(KArgs...), dim3 grid, dim3 block,
   return hipLaunchKernel((const void *)kernel, grid, block, argv, lds, stream);
 }
 
+// The same kernel and arguments as launch(), added as a node of graph g after
+// the n_deps nodes in deps (the node copies the arguments).
+template <typename... KArgs, typename... Args>
+static inline hipError_t add_node(hipGraph_t g, const hipGraphNode_t *deps, size_t n_deps, hipGraphNode_t *node,
+                                  void (*kernel)(KArgs...), dim3 grid, dim3 block, Args... args) {
+  static_assert(sizeof...(KArgs) == sizeof...(Args), "argument count");
+  static_assert((std::is_same<KArgs, Args>::value && ...), "argument types must match the kernel exactly");
+  void *argv[] = {(void *)&args...};
+  hipKernelNodeParams p{};
+  p.func = (void *)kernel;
+  p.gridDim = grid;
+  p.blockDim = block;
+  p.sharedMemBytes = 0;
+  p.kernelParams = argv;
+  p.extra = nullptr;
+  return hipGraphAddKernelNode(node, g, deps, n_deps, &p);
+}
+
 // Runs a set-up call's body and turns a failed host allocation into a status,
 // so that no C++ exception crosses the C interface.
 template <typename F>
@@ -67,6 +85,12 @@ hipError_t launch_pack(const float *src, uint64_t n_elems, uint16_t *ring, uint6
 hipError_t launch_combine(const uint16_t *a, const uint16_t *b, uint64_t n, void *out, int mode,
                           hipStream_t stream);
 hipError_t launch_combine_f32(const float *a, const float *b, uint64_t n, void *out, int mode, hipStream_t stream);
+// The same pack and combine launches as graph nodes (the graph form of the
+// streamed all-reduce).
+hipError_t node_pack(hipGraph_t g, const hipGraphNode_t *deps, size_t n_deps, hipGraphNode_t *node, const float *src,
+                     uint64_t n_elems, uint16_t *ring, uint64_t ring_elems, uint64_t slot0_elem);
+hipError_t node_combine(hipGraph_t g, const hipGraphNode_t *deps, size_t n_deps, hipGraphNode_t *node,
+                        const uint16_t *a, const uint16_t *b, uint64_t n, void *out, int mode);
 
 // ---- argmax (argmax.hip)
 struct ArgmaxShard {

@@ -190,25 +190,58 @@ uint32_t grid_for(uint64_t n_quads) {
 
 }  // namespace
 
-hipError_t launch_pack(const float *src, uint64_t n_elems, uint16_t *ring, uint64_t ring_elems,
-                       uint64_t slot0_elem, hipStream_t stream) {
+// The pack and combine launches, handed to `emit` (an eager launch or a graph
+// node) with their kernel, grid and exact arguments.
+template <typename Emit>
+hipError_t pack_call(Emit &&emit, const float *src, uint64_t n_elems, uint16_t *ring, uint64_t ring_elems,
+                     uint64_t slot0_elem) {
   const uint64_t n_quads = n_elems / 4;
   const uint32_t tail = (uint32_t)(n_elems % 4);
-  return launch(pack_kernel, dim3(grid_for(n_quads)), dim3(kThreads), 0, stream,
-                reinterpret_cast<const uint4 *>(src), reinterpret_cast<uint2 *>(ring), n_quads, ring_elems / 4,
-                slot0_elem / 4, tail);
+  return emit(pack_kernel, dim3(grid_for(n_quads)), dim3(kThreads), reinterpret_cast<const uint4 *>(src),
+              reinterpret_cast<uint2 *>(ring), n_quads, ring_elems / 4, slot0_elem / 4, tail);
 }
 
-hipError_t launch_combine(const uint16_t *a, const uint16_t *b, uint64_t n, void *out, int mode,
-                          hipStream_t stream) {
+template <typename Emit>
+hipError_t combine_call(Emit &&emit, const uint16_t *a, const uint16_t *b, uint64_t n, void *out, int mode) {
   const uint64_t n_quads = n / 4;
   const uint32_t tail = (uint32_t)(n % 4);
   const uint2 *a2 = reinterpret_cast<const uint2 *>(a);
   const uint2 *b2 = reinterpret_cast<const uint2 *>(b);
   const dim3 grid(grid_for(n_quads));
-  if (mode == XFER_OUT_F32)
-    return launch(combine_kernel<XFER_OUT_F32>, grid, dim3(kThreads), 0, stream, a2, b2, out, n_quads, tail);
-  return launch(combine_kernel<XFER_OUT_BF16>, grid, dim3(kThreads), 0, stream, a2, b2, out, n_quads, tail);
+  if (mode == XFER_OUT_F32) return emit(combine_kernel<XFER_OUT_F32>, grid, dim3(kThreads), a2, b2, out, n_quads, tail);
+  return emit(combine_kernel<XFER_OUT_BF16>, grid, dim3(kThreads), a2, b2, out, n_quads, tail);
+}
+
+hipError_t launch_pack(const float *src, uint64_t n_elems, uint16_t *ring, uint64_t ring_elems,
+                       uint64_t slot0_elem, hipStream_t stream) {
+  auto emit = [&](auto kernel, dim3 grid, dim3 block, auto... args) {
+    return launch(kernel, grid, block, 0, stream, args...);
+  };
+  return pack_call(emit, src, n_elems, ring, ring_elems, slot0_elem);
+}
+
+hipError_t launch_combine(const uint16_t *a, const uint16_t *b, uint64_t n, void *out, int mode,
+                          hipStream_t stream) {
+  auto emit = [&](auto kernel, dim3 grid, dim3 block, auto... args) {
+    return launch(kernel, grid, block, 0, stream, args...);
+  };
+  return combine_call(emit, a, b, n, out, mode);
+}
+
+hipError_t node_pack(hipGraph_t g, const hipGraphNode_t *deps, size_t n_deps, hipGraphNode_t *node, const float *src,
+                     uint64_t n_elems, uint16_t *ring, uint64_t ring_elems, uint64_t slot0_elem) {
+  auto emit = [&](auto kernel, dim3 grid, dim3 block, auto... args) {
+    return add_node(g, deps, n_deps, node, kernel, grid, block, args...);
+  };
+  return pack_call(emit, src, n_elems, ring, ring_elems, slot0_elem);
+}
+
+hipError_t node_combine(hipGraph_t g, const hipGraphNode_t *deps, size_t n_deps, hipGraphNode_t *node,
+                        const uint16_t *a, const uint16_t *b, uint64_t n, void *out, int mode) {
+  auto emit = [&](auto kernel, dim3 grid, dim3 block, auto... args) {
+    return add_node(g, deps, n_deps, node, kernel, grid, block, args...);
+  };
+  return combine_call(emit, a, b, n, out, mode);
 }
 
 hipError_t launch_combine_f32(const float *a, const float *b, uint64_t n, void *out, int mode, hipStream_t stream) {

@@ -36,6 +36,7 @@
 // through its PACKED wait.  The first R chunks keep both waits: they order the
 // call after the previous one, which may have used other streams.
 #include <cstring>
+#include <vector>
 
 #include "internal.h"
 
@@ -100,11 +101,68 @@ bool for_each_op(uint32_t n_chunks, uint32_t R, Visit &&visit) {
   return true;
 }
 
+// The graph form's dependencies, for every operation in issue order: the
+// previous operation on its stream, and for each event it waits on, the last
+// operation recorded on that event before it in the same all-reduce (a wait on
+// an event not yet recorded in this all-reduce orders it after an earlier
+// call, which a graph gets from the launch order of its stream instead).
+// visit(op, op index, dependency indices, count).  last_on_stream holds
+// kStreams entries and last_record 6 * R, both scratch.
+template <typename Visit>
+bool for_each_op_deps(uint32_t n_chunks, uint32_t R, int64_t *last_on_stream, int64_t *last_record, Visit &&visit) {
+  for (uint32_t k = 0; k < kStreams; ++k) last_on_stream[k] = -1;
+  for (uint32_t k = 0; k < 6 * R; ++k) last_record[k] = -1;
+  uint64_t i = 0;
+  return for_each_op(n_chunks, R, [&](const xfer_op &op) {
+    uint64_t deps[3];
+    uint32_t nd = 0;
+    auto add = [&](int64_t k) {
+      if (k < 0) return;
+      for (uint32_t j = 0; j < nd; ++j)
+        if (deps[j] == (uint64_t)k) return;
+      deps[nd++] = (uint64_t)k;
+    };
+    add(last_on_stream[op.stream]);
+    for (uint32_t w = 0; w < op.n_waits; ++w) add(last_record[op.wait_event[w]]);
+    if (!visit(op, i, deps, nd)) return false;
+    last_on_stream[op.stream] = (int64_t)i;
+    last_record[op.record_event] = (int64_t)i;
+    ++i;
+    return true;
+  });
+}
+
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
 }  // namespace
 
 extern "C" {
+
+int xfer_allreduce2_graph_deps(uint32_t n_chunks, uint32_t R, uint32_t *from, uint32_t *to, size_t cap,
+                               size_t *n_deps) {
+  if (R == 0 || !n_deps) return XFER_E_INVAL;
+  if (R > UINT32_MAX / 6 || (uint64_t)n_chunks * 6 > UINT32_MAX) return XFER_E_INVAL;
+  return xfer::guarded([&]() -> int {
+    std::vector<int64_t> on_stream(kStreams), record(6ull * R);
+    size_t k = 0;
+    bool room = true;
+    for_each_op_deps(n_chunks, R, on_stream.data(), record.data(),
+                     [&](const xfer_op &, uint64_t i, const uint64_t *deps, uint32_t nd) {
+                       for (uint32_t j = 0; j < nd; ++j, ++k)
+                         if (k < cap && from && to) {
+                           from[k] = (uint32_t)deps[j];
+                           to[k] = (uint32_t)i;
+                         } else if (k >= cap) {
+                           room = false;
+                         }
+                       return true;
+                     });
+    *n_deps = k;
+    if (!room) return XFER_E_RANGE;
+    if (k && (!from || !to)) return XFER_E_INVAL;
+    return XFER_OK;
+  });
+}
 
 uint32_t xfer_allreduce2_event_id(uint32_t kind, uint32_t rank, uint32_t slot, uint32_t R) {
   return event_id(kind, rank, slot, R);
@@ -201,20 +259,51 @@ int check_desc(const xfer_allreduce2_desc *d, Call *c) {
   return XFER_OK;
 }
 
+// Operands of one operation: a pack, a wire copy or a combine.
+struct OpArgs {
+  const float *src;   // PACK: the rank's chunk
+  uint16_t *ring;     // PACK: the rank's send ring
+  uint64_t len;       // elements of the chunk
+  uint64_t soff;      // element offset of the slot
+  const void *from;   // WIRE: send slot; COMBINE: rank 0's operand
+  void *to;           // WIRE: peer's receive slot
+  const uint16_t *a, *b;
+  void *out;          // COMBINE: the rank's output at the chunk
+};
+
+OpArgs op_args(const xfer_allreduce2_desc *d, const Call &c, const xfer_op &op) {
+  OpArgs x{};
+  const uint64_t e0 = (uint64_t)op.chunk * c.ce;
+  x.len = (d->n - e0 < c.ce) ? d->n - e0 : c.ce;
+  x.soff = (uint64_t)op.slot * c.ce;
+  const uint32_t r = op.rank;
+  x.src = d->src[r] + e0;
+  x.ring = d->send[r];
+  x.from = d->send[r] + x.soff;
+  x.to = d->recv[1 - r] + x.soff;
+  // rank 0's value first on both ranks
+  x.a = (r == 0) ? d->send[0] + x.soff : d->recv[1] + x.soff;
+  x.b = (r == 0) ? d->recv[0] + x.soff : d->send[1] + x.soff;
+  x.out = static_cast<uint8_t *>(d->out[r]) + e0 * c.out_esize;
+  return x;
+}
+
 // Enqueue the work of one operation on stream st.
 hipError_t issue(const xfer_allreduce2_desc *d, const Call &c, const xfer_op &op, hipStream_t st) {
-  const uint64_t e0 = (uint64_t)op.chunk * c.ce;
-  const uint64_t len = (d->n - e0 < c.ce) ? d->n - e0 : c.ce;
-  const uint64_t soff = (uint64_t)op.slot * c.ce;  // element offset of the slot
-  const uint32_t r = op.rank;
-  if (op.kind == XFER_OP_PACK) return xfer::launch_pack(d->src[r] + e0, len, d->send[r], c.R * c.ce, soff, st);
+  const OpArgs x = op_args(d, c, op);
+  if (op.kind == XFER_OP_PACK) return xfer::launch_pack(x.src, x.len, x.ring, c.R * c.ce, x.soff, st);
+  if (op.kind == XFER_OP_WIRE) return hipMemcpyAsync(x.to, x.from, x.len * 2, hipMemcpyDeviceToDevice, st);
+  return xfer::launch_combine(x.a, x.b, x.len, x.out, d->out_mode, st);
+}
+
+// The same operation as a node of graph g after the given nodes.
+hipError_t add_op_node(hipGraph_t g, const hipGraphNode_t *deps, size_t nd, hipGraphNode_t *node,
+                       const xfer_allreduce2_desc *d, const Call &c, const xfer_op &op) {
+  const OpArgs x = op_args(d, c, op);
+  if (op.kind == XFER_OP_PACK) return xfer::node_pack(g, deps, nd, node, x.src, x.len, x.ring, c.R * c.ce, x.soff);
   if (op.kind == XFER_OP_WIRE)
-    return hipMemcpyAsync(d->recv[1 - r] + soff, d->send[r] + soff, len * 2, hipMemcpyDeviceToDevice, st);
-  // rank 0's value first on both ranks
-  const uint16_t *a = (r == 0) ? d->send[0] + soff : d->recv[1] + soff;
-  const uint16_t *b = (r == 0) ? d->recv[0] + soff : d->send[1] + soff;
-  void *o = static_cast<uint8_t *>(d->out[r]) + e0 * c.out_esize;
-  return xfer::launch_combine(a, b, len, o, d->out_mode, st);
+    return hipGraphAddMemcpyNode1D(node, g, deps, nd, x.to, x.from, x.len * 2, hipMemcpyDeviceToDevice);
+  return xfer::node_combine(g, deps, nd, node, x.a, x.b, x.len, x.out, d->out_mode);
 }
 
 }  // namespace
@@ -246,11 +335,29 @@ int xfer_allreduce2_graph_create(const xfer_allreduce2_desc *d, hipGraphExec_t *
   Call c;
   const int st0 = check_desc(d, &c);
   if (st0 != XFER_OK || c.n_chunks == 0) return st0;
-  // Recording the schedule by stream capture on private streams crashed the
-  // host process inside this call on MI355X (ROCm 7.2) and the cause is not
-  // found, so building the graph is switched off: every non-empty call is
-  // refused before any runtime call.
-  return XFER_E_UNSUPPORTED;
+  if (6 * c.n_chunks > UINT32_MAX) return XFER_E_INVAL;
+  // Nodes with explicit dependencies; no stream capture, and the descriptor's
+  // streams and events are not used.
+  return xfer::guarded([&]() -> int {
+    std::vector<hipGraphNode_t> nodes(6 * c.n_chunks, nullptr);
+    std::vector<int64_t> on_stream(kStreams), record(6 * c.R);
+    hipGraph_t g = nullptr;
+    if (hipGraphCreate(&g, 0) != hipSuccess) return XFER_E_DEVICE;
+    hipError_t err = hipSuccess;
+    for_each_op_deps((uint32_t)c.n_chunks, (uint32_t)c.R, on_stream.data(), record.data(),
+                     [&](const xfer_op &op, uint64_t i, const uint64_t *deps, uint32_t nd) {
+                       hipGraphNode_t dn[3];
+                       for (uint32_t j = 0; j < nd; ++j) dn[j] = nodes[deps[j]];
+                       err = add_op_node(g, dn, nd, &nodes[i], d, c, op);
+                       return err == hipSuccess;
+                     });
+    hipGraphExec_t e = nullptr;
+    if (err == hipSuccess) err = hipGraphInstantiateWithFlags(&e, g, 0);
+    (void)hipGraphDestroy(g);  // the executable graph keeps what it needs
+    if (err != hipSuccess) return XFER_E_DEVICE;
+    *exec = e;
+    return XFER_OK;
+  });
 }
 
 int xfer_allreduce2_graph_launch(hipGraphExec_t exec, hipStream_t stream) {

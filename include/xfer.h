@@ -603,20 +603,38 @@ typedef struct {
 XFER_API int xfer_allreduce2_streamed(const xfer_allreduce2_desc *d);
 
 /*
- * xfer_allreduce2_graph_create - the same schedule recorded once as a HIP
- * graph over the descriptor's buffers, so that a whole all-reduce costs one
- * launch (the streamed call makes three to four runtime calls per
- * operation and is bound by them at 512 KiB chunks).
- * SWITCHED OFF: recording the schedule by stream capture crashed the host
- * process inside this call on MI355X (ROCm 7.2), cause not found.  The call
- * checks its arguments like xfer_allreduce2_streamed (XFER_E_INVAL, NULL exec
- * included), sets *exec to NULL, returns XFER_OK when n == 0 (nothing to
- * do) and XFER_E_UNSUPPORTED otherwise, without any runtime call.
+ * xfer_allreduce2_graph_create - the same all-reduce built once as a HIP graph
+ * over the descriptor's buffers, so that a whole all-reduce costs one launch
+ * (the streamed call makes three to four runtime calls per operation and is
+ * bound by them at 512 KiB chunks).  Every operation of the schedule becomes
+ * a node: a pack or combine kernel node, or a device-to-device copy node for
+ * the wire.  Its dependencies are the ones xfer_allreduce2_graph_deps lists:
+ * the previous operation on its stream and, for each event it waits on, the
+ * operation that last recorded that event earlier in the all-reduce.  There is
+ * no stream capture: d->compute, d->wire, d->events and d->n_events are not
+ * used (they may be NULL / 0).  The graph holds the buffer addresses; the
+ * caller keeps the buffers alive and unmoved while the graph exists.
+ * Launches on one stream run one after the other; launches on different
+ * streams that share buffers must be ordered by the caller.
+ * Errors: those of xfer_allreduce2_streamed's descriptor checks (XFER_E_INVAL,
+ * a NULL exec included); XFER_E_DEVICE if the runtime refuses a node or the
+ * instantiation; XFER_E_HOST_MEMORY if host scratch cannot be allocated.
+ * n == 0: XFER_OK and *exec = NULL (nothing to launch).  Set-up call: it
+ * allocates host memory and runtime objects.
  *
  * xfer_allreduce2_graph_launch - enqueue one all-reduce on stream (a NULL
  * exec is a no-op).  xfer_allreduce2_graph_destroy - release the graph (NULL
  * is a no-op).
+ *
+ * xfer_allreduce2_graph_deps - the graph form's dependency list for n_chunks
+ * chunks and R slots, host only: dependency k says operation to[k] (an index
+ * into xfer_allreduce2_schedule's list) runs after operation from[k].  from
+ * and to (host) have capacity cap; *n_deps receives the count.  Errors:
+ * XFER_E_INVAL for R == 0 or NULL n_deps, XFER_E_RANGE if cap is too small
+ * (from and to may then be NULL with cap 0, to ask for the count).
  */
+XFER_API int xfer_allreduce2_graph_deps(uint32_t n_chunks, uint32_t R, uint32_t *from, uint32_t *to, size_t cap,
+                                        size_t *n_deps);
 XFER_API int xfer_allreduce2_graph_create(const xfer_allreduce2_desc *d, hipGraphExec_t *exec);
 XFER_API int xfer_allreduce2_graph_launch(hipGraphExec_t exec, hipStream_t stream);
 XFER_API int xfer_allreduce2_graph_destroy(hipGraphExec_t exec);

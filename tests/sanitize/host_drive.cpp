@@ -381,9 +381,62 @@ void streamed(Rng &g) {
     d.n_events = ev.size();
     CHECK(xfer_allreduce2_streamed(&d) == XFER_OK);
     CHECK(xfer_allreduce2_streamed(&d) == XFER_OK);  // a second call on the same rings and events
-    hipGraphExec_t ex = reinterpret_cast<hipGraphExec_t>((uintptr_t)1);
-    CHECK(xfer_allreduce2_graph_create(&d, &ex) == (n ? XFER_E_UNSUPPORTED : XFER_OK));
-    CHECK(ex == nullptr);
+    // The graph form: built without the descriptor's streams and events.
+    {
+      xfer_allreduce2_desc gd = d;
+      gd.events = nullptr;
+      gd.n_events = 0;
+      gd.compute[0] = gd.compute[1] = gd.wire[0] = gd.wire[1] = nullptr;
+      hipGraphExec_t ex = reinterpret_cast<hipGraphExec_t>((uintptr_t)1);
+      mock::g_last_graph.clear();
+      CHECK(xfer_allreduce2_graph_create(&gd, &ex) == XFER_OK);
+      CHECK((ex == nullptr) == (n == 0));
+      CHECK(mock::g_live_graphs == 0);  // only the executable graph is kept
+      if (n) {
+        const uint64_t ce = chunk / 2, n_chunks = (n + ce - 1) / ce;
+        std::vector<xfer_op> ops(6 * n_chunks);
+        size_t n_ops = 0;
+        CHECK(xfer_allreduce2_schedule((uint32_t)n_chunks, R, ops.data(), ops.size(), &n_ops) == XFER_OK);
+        size_t n_deps = 0;
+        CHECK(xfer_allreduce2_graph_deps((uint32_t)n_chunks, R, nullptr, nullptr, 0, &n_deps) ==
+              (n_ops > 1 ? XFER_E_RANGE : XFER_OK));
+        std::vector<uint32_t> from(n_deps + 1), to(n_deps + 1);
+        CHECK(xfer_allreduce2_graph_deps((uint32_t)n_chunks, R, from.data(), to.data(), from.size(), &n_deps) ==
+              XFER_OK);
+        // one node per operation, of its kind and size, with exactly the listed dependencies
+        const std::vector<mock::GraphNodeLog> &gl = mock::g_last_graph;
+        CHECK(gl.size() == n_ops);
+        std::vector<std::vector<uint32_t>> want(n_ops);
+        for (size_t k = 0; k < n_deps; ++k) {
+          CHECK(from[k] < to[k]);  // a dependency always points back in issue order
+          want[to[k]].push_back(from[k]);
+        }
+        for (size_t i = 0; i < n_ops; ++i) {
+          CHECK(gl[i].kind == (int)ops[i].kind);
+          const uint64_t e0 = (uint64_t)ops[i].chunk * ce, len = std::min<uint64_t>(ce, n - e0);
+          CHECK(gl[i].n == (ops[i].kind == XFER_OP_WIRE ? 2 * len : len));
+          std::vector<uint32_t> a = gl[i].deps, b = want[i];
+          std::sort(a.begin(), a.end());
+          std::sort(b.begin(), b.end());
+          CHECK(a == b);
+        }
+        const long launches = mock::g_graph_launches;
+        CHECK(xfer_allreduce2_graph_launch(ex, token(15)) == XFER_OK);
+        CHECK(mock::g_graph_launches == launches + 1);
+        CHECK(xfer_allreduce2_graph_destroy(ex) == XFER_OK);
+        // a refused node or instantiation: nothing is kept
+        mock::fail_graph_node_at((int)g.below(n_ops));
+        CHECK(xfer_allreduce2_graph_create(&gd, &ex) == XFER_E_DEVICE);
+        CHECK(ex == nullptr);
+        mock::reset_failures();
+        mock::fail_instantiate(true);
+        CHECK(xfer_allreduce2_graph_create(&gd, &ex) == XFER_E_DEVICE);
+        CHECK(ex == nullptr);
+        mock::reset_failures();
+      }
+      CHECK(mock::g_live_graphs == 0 && mock::g_live_execs == 0);
+      CHECK(xfer_allreduce2_graph_create(&gd, nullptr) == XFER_E_INVAL);
+    }
     d.recv[1] = d.send[0];  // rings that alias
     CHECK(xfer_allreduce2_streamed(&d) == (n ? XFER_E_INVAL : XFER_OK));
     CHECK(xfer_events_destroy(ev.data(), (int)ev.size()) == XFER_OK);

@@ -21,6 +21,9 @@ int g_memcpy_calls = 0;
 int g_fail_memcpy_at = -1;
 bool g_fail_launches = false;
 bool g_fail_scratch = false;
+int g_node_calls = 0;
+int g_fail_node_at = -1;
+bool g_fail_instantiate = false;
 
 [[noreturn]] void die(const char *what) {
   std::fprintf(stderr, "mock hip: %s\n", what);
@@ -41,9 +44,16 @@ void reset_failures() {
   g_create_calls = g_record_calls = g_memcpy_calls = 0;
   g_fail_launches = false;
   g_fail_scratch = false;
+  g_fail_node_at = -1;
+  g_node_calls = 0;
+  g_fail_instantiate = false;
 }
 void fail_launches(bool on) { g_fail_launches = on; }
 void fail_scratch(bool on) { g_fail_scratch = on; }
+std::vector<GraphNodeLog> g_last_graph;
+long g_live_graphs = 0, g_live_execs = 0, g_graph_launches = 0;
+void fail_graph_node_at(int k) { g_node_calls = 0; g_fail_node_at = k; }
+void fail_instantiate(bool on) { g_fail_instantiate = on; }
 void fail_event_create_at(int k) { g_create_calls = 0; g_fail_create_at = k; }
 void fail_event_record_at(int k) { g_record_calls = 0; g_fail_record_at = k; }
 void fail_memcpy_at(int k) { g_memcpy_calls = 0; g_fail_memcpy_at = k; }
@@ -99,8 +109,104 @@ hipError_t hipStreamWaitEvent(hipStream_t, hipEvent_t event, unsigned) {
   return hipSuccess;
 }
 
-hipError_t hipGraphLaunch(hipGraphExec_t, hipStream_t) { die("graph launch reached"); }
-hipError_t hipGraphExecDestroy(hipGraphExec_t) { die("graph destroy reached"); }
+}  // extern "C"
+
+// ---- graphs: nodes are recorded with their dependencies
+struct hipGraphNode {
+  uint32_t index;
+};
+struct ihipGraph {
+  std::vector<hipGraphNode *> nodes;
+  std::vector<mock::GraphNodeLog> log;
+};
+struct hipGraphExec {
+  std::vector<mock::GraphNodeLog> log;
+};
+
+namespace {
+hipError_t add_logged(hipGraphNode_t *node, hipGraph_t g, const hipGraphNode_t *deps, size_t n_deps, int kind,
+                      uint64_t n) {
+  if (!node || !g) die("graph node: NULL node slot or graph");
+  if (n_deps && !deps) die("graph node: NULL dependencies");
+  if (g_node_calls++ == g_fail_node_at) return hipErrorInvalidValue;
+  mock::GraphNodeLog rec{kind, {}, n};
+  for (size_t j = 0; j < n_deps; ++j) {
+    if (!deps[j]) die("graph node: NULL dependency");
+    bool found = false;
+    for (hipGraphNode *m : g->nodes) found |= (m == deps[j]);
+    if (!found) die("graph node: a dependency from another graph or unknown");
+    rec.deps.push_back(deps[j]->index);
+  }
+  hipGraphNode *nd = new hipGraphNode{(uint32_t)g->nodes.size()};
+  g->nodes.push_back(nd);
+  g->log.push_back(rec);
+  *node = nd;
+  return hipSuccess;
+}
+}  // namespace
+
+namespace mock {
+hipError_t add_node_for_test(hipGraphNode_t *node, hipGraph_t g, const hipGraphNode_t *deps, size_t n_deps, int kind,
+                             uint64_t n) {
+  return add_logged(node, g, deps, n_deps, kind, n);
+}
+}  // namespace mock
+
+extern "C" {
+
+hipError_t hipGraphCreate(hipGraph_t *graph, unsigned) {
+  if (!graph) die("graph create: NULL slot");
+  *graph = new ihipGraph;
+  ++mock::g_live_graphs;
+  return hipSuccess;
+}
+
+hipError_t hipGraphDestroy(hipGraph_t graph) {
+  if (!graph) die("graph destroy: NULL");
+  for (hipGraphNode *n : graph->nodes) delete n;
+  delete graph;
+  --mock::g_live_graphs;
+  return hipSuccess;
+}
+
+hipError_t hipGraphAddMemcpyNode1D(hipGraphNode_t *node, hipGraph_t graph, const hipGraphNode_t *deps, size_t n_deps,
+                                   void *dst, const void *src, size_t bytes, hipMemcpyKind kind) {
+  if (kind != hipMemcpyDeviceToDevice) die("graph copy: unexpected kind");
+  if (bytes && (!dst || !src)) die("graph copy: NULL operand");
+  if (bytes) {  // the operands must hold `bytes` bytes
+    const volatile uint8_t *d = static_cast<const volatile uint8_t *>(dst);
+    const volatile uint8_t *s = static_cast<const volatile uint8_t *>(src);
+    (void)(d[0] ^ d[bytes - 1] ^ s[0] ^ s[bytes - 1]);
+  }
+  return add_logged(node, graph, deps, n_deps, 1, bytes);
+}
+
+hipError_t hipGraphAddKernelNode(hipGraphNode_t *, hipGraph_t, const hipGraphNode_t *, size_t,
+                                 const hipKernelNodeParams *) {
+  die("direct kernel node");
+}
+
+hipError_t hipGraphInstantiateWithFlags(hipGraphExec_t *exec, hipGraph_t graph, unsigned long long) {
+  if (!exec || !graph) die("instantiate: NULL");
+  if (g_fail_instantiate) return hipErrorInvalidValue;
+  *exec = new hipGraphExec{graph->log};
+  mock::g_last_graph = graph->log;
+  ++mock::g_live_execs;
+  return hipSuccess;
+}
+
+hipError_t hipGraphLaunch(hipGraphExec_t exec, hipStream_t) {
+  if (!exec) die("graph launch: NULL");
+  ++mock::g_graph_launches;
+  return hipSuccess;
+}
+
+hipError_t hipGraphExecDestroy(hipGraphExec_t exec) {
+  if (!exec) die("graph exec destroy: NULL");
+  delete exec;
+  --mock::g_live_execs;
+  return hipSuccess;
+}
 
 }  // extern "C"
 
@@ -138,6 +244,22 @@ hipError_t launch_combine(const uint16_t *a, const uint16_t *b, uint64_t n, void
   touch(b, n * 2);
   touch(out, n * (mode == XFER_OUT_F32 ? 4 : 2));
   return note("combine", n, (uint64_t)mode, 0);
+}
+
+hipError_t node_pack(hipGraph_t g, const hipGraphNode_t *deps, size_t n_deps, hipGraphNode_t *node, const float *src,
+                     uint64_t n, uint16_t *ring, uint64_t ring_elems, uint64_t slot0) {
+  if (slot0 >= ring_elems) die("pack node: slot outside the ring");
+  touch(src, n * 4);
+  touch(ring, ring_elems * 2);
+  return mock::add_node_for_test(node, g, deps, n_deps, 0, n);
+}
+
+hipError_t node_combine(hipGraph_t g, const hipGraphNode_t *deps, size_t n_deps, hipGraphNode_t *node,
+                        const uint16_t *a, const uint16_t *b, uint64_t n, void *out, int mode) {
+  touch(a, n * 2);
+  touch(b, n * 2);
+  touch(out, n * (mode == XFER_OUT_F32 ? 4 : 2));
+  return mock::add_node_for_test(node, g, deps, n_deps, 2, n);
 }
 
 hipError_t launch_combine_f32(const float *a, const float *b, uint64_t n, void *out, int mode, hipStream_t) {

@@ -24,6 +24,8 @@ typedef enum hipError_t {
 typedef struct ihipStream_t *hipStream_t;
 typedef struct ihipEvent_t *hipEvent_t;
 typedef struct hipGraphExec *hipGraphExec_t;
+typedef struct ihipGraph *hipGraph_t;
+typedef struct hipGraphNode *hipGraphNode_t;
 
 typedef enum hipMemcpyKind {
   hipMemcpyHostToHost = 0,
@@ -40,6 +42,14 @@ struct dim3 {
   uint32_t x, y, z;
   dim3(uint32_t x_ = 1, uint32_t y_ = 1, uint32_t z_ = 1) : x(x_), y(y_), z(z_) {}
 };
+typedef struct hipKernelNodeParams {
+  dim3 blockDim;
+  void **extra;
+  void *func;
+  dim3 gridDim;
+  void **kernelParams;
+  unsigned int sharedMemBytes;
+} hipKernelNodeParams;
 extern "C" {
 #endif
 
@@ -52,6 +62,15 @@ hipError_t hipEventSynchronize(hipEvent_t event);
 hipError_t hipStreamWaitEvent(hipStream_t stream, hipEvent_t event, unsigned flags);
 hipError_t hipGraphLaunch(hipGraphExec_t exec, hipStream_t stream);
 hipError_t hipGraphExecDestroy(hipGraphExec_t exec);
+hipError_t hipGraphCreate(hipGraph_t *graph, unsigned flags);
+hipError_t hipGraphDestroy(hipGraph_t graph);
+hipError_t hipGraphAddMemcpyNode1D(hipGraphNode_t *node, hipGraph_t graph, const hipGraphNode_t *deps, size_t n_deps,
+                                   void *dst, const void *src, size_t bytes, hipMemcpyKind kind);
+hipError_t hipGraphInstantiateWithFlags(hipGraphExec_t *exec, hipGraph_t graph, unsigned long long flags);
+#ifdef __cplusplus
+hipError_t hipGraphAddKernelNode(hipGraphNode_t *node, hipGraph_t graph, const hipGraphNode_t *deps, size_t n_deps,
+                                 const hipKernelNodeParams *params);
+#endif
 #ifdef __cplusplus
 hipError_t hipLaunchKernel(const void *function, dim3 grid, dim3 block, void **args, size_t lds, hipStream_t stream);
 #endif

@@ -145,10 +145,6 @@ def test_prompt_batch_2048x5120_two_512k_slots():
     assert np.array_equal(down(outs[1], np.uint32), want)
 
 
-GRAPH_OFF = "recording the schedule as a HIP graph crashed the host process inside xfer_allreduce2_graph_create on MI355X (ROCm 7.2), twice; the builder is switched off (it returns XFER_E_UNSUPPORTED) until a cause is found"
-
-
-@pytest.mark.skip(reason=GRAPH_OFF)
 @pytest.mark.parametrize("R", [1, 2, 3])
 @pytest.mark.parametrize("mode", [x.OUT_F32, x.OUT_BF16])
 def test_graph_small_chunks_repeated_launches(R, mode):
@@ -178,7 +174,6 @@ def test_graph_small_chunks_repeated_launches(R, mode):
     g.close()
 
 
-@pytest.mark.skip(reason=GRAPH_OFF)
 def test_graph_prompt_batch_2048x5120():
     n, chunk, R = 2048 * 5120, 512 * 1024, 2
     a = dg.prompt_partial(n, dg.seed_for(2, 0, 2048))

@@ -26,10 +26,10 @@ def _accesses(op):
     return [(("send", r, s), False), (("recv", r, s), False), (("out", r, op["chunk"]), True)]
 
 
-def _happens_before(ops):
-    """hb[i] = set of ops that happen before op i (transitively)."""
-    n = len(ops)
-    preds = [set() for _ in range(n)]
+def _direct_preds(ops):
+    """preds[i] = the ops op i is directly ordered after: its stream's previous
+    op and the last recorder of each event it waits on."""
+    preds = [set() for _ in ops]
     last_on_stream = {}
     last_record = {}
     for i, op in enumerate(ops):
@@ -40,6 +40,12 @@ def _happens_before(ops):
                 preds[i].add(last_record[e])
         last_on_stream[op["stream"]] = i
         last_record[op["record"]] = i
+    return preds
+
+
+def _closure(preds):
+    """hb[i] = set of ops that happen before op i (transitively)."""
+    n = len(preds)
     hb = []
     for i in range(n):
         s = set()
@@ -50,8 +56,12 @@ def _happens_before(ops):
     return hb
 
 
-def _hazards(ops):
-    hb = _happens_before(ops)
+def _happens_before(ops):
+    return _closure(_direct_preds(ops))
+
+
+def _hazards(ops, hb=None):
+    hb = _happens_before(ops) if hb is None else hb
     acc = [_accesses(o) for o in ops]
     bad = []
     for j in range(len(ops)):
@@ -176,13 +186,68 @@ def test_graph_builder_argument_checks():
     assert x.lib().xfer_allreduce2_graph_create(ctypes.byref(empty), ctypes.byref(ex)) == x.OK
     assert ex.value is None
     assert x.lib().xfer_allreduce2_graph_create(ctypes.byref(d), None) == x.E_INVAL
-    # switched off: a valid non-empty call is refused before any runtime call
-    assert x.allreduce2_graph_create_status(d) == x.E_UNSUPPORTED
     assert x.lib().xfer_allreduce2_graph_launch(None, None) == x.OK
     assert x.lib().xfer_allreduce2_graph_destroy(None) == x.OK
     no_events = x.AllReduce2Desc.from_buffer_copy(d)
     no_events.events = None
     assert x.lib().xfer_allreduce2_streamed(ctypes.byref(no_events)) == x.E_INVAL
+
+
+@pytest.mark.parametrize("R", [1, 2, 3, 4])
+@pytest.mark.parametrize("n_chunks", [1, 2, 3, 5, 9])
+def test_graph_dependencies_are_the_streams_orderings(R, n_chunks):
+    """The graph form gives each operation exactly the edges its stream and
+    event waits give it in the streamed call, so it runs no pair of
+    conflicting operations unordered; and every edge points back in issue order."""
+    ops = x.allreduce2_schedule(n_chunks, R)
+    deps = x.allreduce2_graph_deps(n_chunks, R)
+    assert len(deps) == len(set(deps))
+    preds = [set() for _ in ops]
+    for a, b in deps:
+        assert 0 <= a < b < len(ops)
+        preds[b].add(a)
+    assert preds == _direct_preds(ops)
+    assert _hazards(ops, _closure(preds)) == []
+
+
+def test_graph_dependency_edges_are_load_bearing():
+    """With one slot, dropping any graph edge that stands for an event wait
+    lets two conflicting operations run unordered (stream-order edges may be
+    implied by the waits)."""
+    R, n_chunks = 1, 4
+    ops = x.allreduce2_schedule(n_chunks, R)
+    deps = x.allreduce2_graph_deps(n_chunks, R)
+    stream_prev = {}
+    last_on_stream = {}
+    for i, op in enumerate(ops):
+        if op["stream"] in last_on_stream:
+            stream_prev[i] = last_on_stream[op["stream"]]
+        last_on_stream[op["stream"]] = i
+    checked = 0
+    for k, (a, b) in enumerate(deps):
+        if stream_prev.get(b) == a:
+            continue
+        preds = [set() for _ in ops]
+        for kk, (aa, bb) in enumerate(deps):
+            if kk != k:
+                preds[bb].add(aa)
+        assert _hazards(ops, _closure(preds)), (a, b)
+        checked += 1
+    assert checked >= 15
+
+
+def test_graph_deps_argument_checks():
+    import ctypes
+    n = ctypes.c_size_t(0)
+    L = x.lib()
+    assert L.xfer_allreduce2_graph_deps(3, 0, None, None, 0, ctypes.byref(n)) == x.E_INVAL
+    assert L.xfer_allreduce2_graph_deps(3, 2, None, None, 0, None) == x.E_INVAL
+    assert L.xfer_allreduce2_graph_deps(3, 2, None, None, 0, ctypes.byref(n)) == x.E_RANGE
+    need = n.value
+    assert need == len(x.allreduce2_graph_deps(3, 2))
+    buf = (ctypes.c_uint32 * need)()
+    assert L.xfer_allreduce2_graph_deps(3, 2, buf, None, need, ctypes.byref(n)) == x.E_INVAL
+    assert L.xfer_allreduce2_graph_deps(0, 2, None, None, 0, ctypes.byref(n)) == x.OK and n.value == 0
 
 
 def _accesses_call(op, call):
