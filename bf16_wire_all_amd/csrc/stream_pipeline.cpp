@@ -106,14 +106,22 @@ bool for_each_op(uint32_t n_chunks, uint32_t R, Visit &&visit) {
 // operation recorded on that event before it in the same all-reduce (a wait on
 // an event not yet recorded in this all-reduce orders it after an earlier
 // call, which a graph gets from the launch order of its stream instead).
-// visit(op, op index, dependency indices, count).  last_on_stream holds
-// kStreams entries and last_record 6 * R, both scratch.
+// visit(op, op index, dependency indices, count).
+//
+// With more slots than chunks (R > n_chunks) every chunk is among the first R
+// and takes slot c either way, so the edges are those of R = n_chunks; the
+// operations are generated with that R, which keeps the host table of last
+// recorders at 6 * min(R, n_chunks) entries (the visited event ids are then
+// numbered for that R; the kinds, ranks, chunks and slots are unchanged).
+// Allocates that table (the callers run inside xfer::guarded).
 template <typename Visit>
-bool for_each_op_deps(uint32_t n_chunks, uint32_t R, int64_t *last_on_stream, int64_t *last_record, Visit &&visit) {
+bool for_each_op_deps(uint32_t n_chunks, uint32_t R, Visit &&visit) {
+  const uint32_t Re = (n_chunks != 0 && R > n_chunks) ? n_chunks : R;
+  int64_t last_on_stream[kStreams];
   for (uint32_t k = 0; k < kStreams; ++k) last_on_stream[k] = -1;
-  for (uint32_t k = 0; k < 6 * R; ++k) last_record[k] = -1;
+  std::vector<int64_t> last_record(6ull * Re, -1);
   uint64_t i = 0;
-  return for_each_op(n_chunks, R, [&](const xfer_op &op) {
+  return for_each_op(n_chunks, Re, [&](const xfer_op &op) {
     uint64_t deps[3];
     uint32_t nd = 0;
     auto add = [&](int64_t k) {
@@ -143,11 +151,9 @@ int xfer_allreduce2_graph_deps(uint32_t n_chunks, uint32_t R, uint32_t *from, ui
   if (R == 0 || !n_deps) return XFER_E_INVAL;
   if (R > UINT32_MAX / 6 || (uint64_t)n_chunks * 6 > UINT32_MAX) return XFER_E_INVAL;
   return xfer::guarded([&]() -> int {
-    std::vector<int64_t> on_stream(kStreams), record(6ull * R);
     size_t k = 0;
     bool room = true;
-    for_each_op_deps(n_chunks, R, on_stream.data(), record.data(),
-                     [&](const xfer_op &, uint64_t i, const uint64_t *deps, uint32_t nd) {
+    for_each_op_deps(n_chunks, R, [&](const xfer_op &, uint64_t i, const uint64_t *deps, uint32_t nd) {
                        for (uint32_t j = 0; j < nd; ++j, ++k)
                          if (k < cap && from && to) {
                            from[k] = (uint32_t)deps[j];
@@ -340,11 +346,16 @@ int xfer_allreduce2_graph_create(const xfer_allreduce2_desc *d, hipGraphExec_t *
   // streams and events are not used.
   return xfer::guarded([&]() -> int {
     std::vector<hipGraphNode_t> nodes(6 * c.n_chunks, nullptr);
-    std::vector<int64_t> on_stream(kStreams), record(6 * c.R);
-    hipGraph_t g = nullptr;
-    if (hipGraphCreate(&g, 0) != hipSuccess) return XFER_E_DEVICE;
+    struct Owned {  // the graph is released on every way out, a host allocation failure included
+      hipGraph_t g = nullptr;
+      ~Owned() {
+        if (g) (void)hipGraphDestroy(g);
+      }
+    } owned;
+    if (hipGraphCreate(&owned.g, 0) != hipSuccess) return XFER_E_DEVICE;
+    hipGraph_t g = owned.g;
     hipError_t err = hipSuccess;
-    for_each_op_deps((uint32_t)c.n_chunks, (uint32_t)c.R, on_stream.data(), record.data(),
+    for_each_op_deps((uint32_t)c.n_chunks, (uint32_t)c.R,
                      [&](const xfer_op &op, uint64_t i, const uint64_t *deps, uint32_t nd) {
                        hipGraphNode_t dn[3];
                        for (uint32_t j = 0; j < nd; ++j) dn[j] = nodes[deps[j]];
@@ -353,8 +364,7 @@ int xfer_allreduce2_graph_create(const xfer_allreduce2_desc *d, hipGraphExec_t *
                      });
     hipGraphExec_t e = nullptr;
     if (err == hipSuccess) err = hipGraphInstantiateWithFlags(&e, g, 0);
-    (void)hipGraphDestroy(g);  // the executable graph keeps what it needs
-    if (err != hipSuccess) return XFER_E_DEVICE;
+    if (err != hipSuccess) return XFER_E_DEVICE;  // the executable graph keeps what it needs of g
     *exec = e;
     return XFER_OK;
   });

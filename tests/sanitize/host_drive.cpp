@@ -433,6 +433,41 @@ void streamed(Rng &g) {
         CHECK(xfer_allreduce2_graph_create(&gd, &ex) == XFER_E_DEVICE);
         CHECK(ex == nullptr);
         mock::reset_failures();
+        // a host allocation failing at each point of the build in turn:
+        // XFER_E_HOST_MEMORY, and the graph made so far is released
+        static bool host_failures_done = false;
+        if (!host_failures_done) {
+          host_failures_done = true;
+          long k = 0;
+          for (;; ++k) {
+            mock::fail_new_after(k);
+            hipGraphExec_t e2 = reinterpret_cast<hipGraphExec_t>((uintptr_t)1);
+            const int st = xfer_allreduce2_graph_create(&gd, &e2);
+            const bool thrown = !mock::new_failure_pending();
+            mock::fail_new_after(-1);
+            if (!thrown) {
+              CHECK(st == XFER_OK && e2 != nullptr);
+              CHECK(xfer_allreduce2_graph_destroy(e2) == XFER_OK);
+              break;
+            }
+            CHECK(st == XFER_E_HOST_MEMORY && e2 == nullptr);
+            CHECK(mock::g_live_graphs == 0 && mock::g_live_execs == 0);
+          }
+          CHECK(k >= 2);  // the node list, and the last-recorder table after the graph exists
+          for (k = 0;; ++k) {  // the same for the dependency list
+            mock::fail_new_after(k);
+            size_t nd2 = 0;
+            const int st = xfer_allreduce2_graph_deps((uint32_t)n_chunks, R, from.data(), to.data(), from.size(), &nd2);
+            const bool thrown = !mock::new_failure_pending();
+            mock::fail_new_after(-1);
+            if (!thrown) {
+              CHECK(st == XFER_OK && nd2 == n_deps);
+              break;
+            }
+            CHECK(st == XFER_E_HOST_MEMORY);
+          }
+          CHECK(k >= 1);
+        }
       }
       CHECK(mock::g_live_graphs == 0 && mock::g_live_execs == 0);
       CHECK(xfer_allreduce2_graph_create(&gd, nullptr) == XFER_E_INVAL);

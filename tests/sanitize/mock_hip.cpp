@@ -6,6 +6,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <new>
 #include <set>
 
 #include "internal.h"
@@ -24,6 +25,15 @@ bool g_fail_scratch = false;
 int g_node_calls = 0;
 int g_fail_node_at = -1;
 bool g_fail_instantiate = false;
+long g_new_countdown = -1;  // host allocations by the code under test before one fails, -1 none
+int g_new_suspended = 0;    // inside the mock runtime, whose own allocations never fail
+
+// The mock runtime's own bookkeeping allocates; a failure injected for the
+// library's host code must not land there.
+struct MockBookkeeping {
+  MockBookkeeping() { ++g_new_suspended; }
+  ~MockBookkeeping() { --g_new_suspended; }
+};
 
 [[noreturn]] void die(const char *what) {
   std::fprintf(stderr, "mock hip: %s\n", what);
@@ -34,6 +44,22 @@ void check_event(hipEvent_t e) {
   if (!g_events.count(e)) die("unknown or destroyed event");
 }
 }  // namespace
+
+// Every scalar new of the program goes through here, so a test can make the
+// k-th allocation of the library's host code fail (std::bad_alloc).
+void *operator new(std::size_t n) {
+  if (g_new_countdown >= 0 && g_new_suspended == 0) {
+    if (g_new_countdown == 0) {
+      g_new_countdown = -1;
+      throw std::bad_alloc();
+    }
+    --g_new_countdown;
+  }
+  if (void *p = std::malloc(n ? n : 1)) return p;
+  throw std::bad_alloc();
+}
+void operator delete(void *p) noexcept { std::free(p); }
+void operator delete(void *p, std::size_t) noexcept { std::free(p); }
 
 namespace mock {
 LaunchLog g_last;
@@ -54,6 +80,8 @@ std::vector<GraphNodeLog> g_last_graph;
 long g_live_graphs = 0, g_live_execs = 0, g_graph_launches = 0;
 void fail_graph_node_at(int k) { g_node_calls = 0; g_fail_node_at = k; }
 void fail_instantiate(bool on) { g_fail_instantiate = on; }
+void fail_new_after(long k) { g_new_countdown = k; }
+bool new_failure_pending() { return g_new_countdown >= 0; }
 void fail_event_create_at(int k) { g_create_calls = 0; g_fail_create_at = k; }
 void fail_event_record_at(int k) { g_record_calls = 0; g_fail_record_at = k; }
 void fail_memcpy_at(int k) { g_memcpy_calls = 0; g_fail_memcpy_at = k; }
@@ -78,6 +106,7 @@ hipError_t hipMemcpyAsync(void *dst, const void *src, size_t bytes, hipMemcpyKin
 }
 
 hipError_t hipEventCreateWithFlags(hipEvent_t *event, unsigned) {
+  MockBookkeeping bookkeeping;
   if (!event) die("NULL event slot");
   if (g_create_calls++ == g_fail_create_at) return hipErrorOutOfMemory;  // leaves *event as it was
   hipEvent_t e = reinterpret_cast<hipEvent_t>(std::malloc(16));
@@ -87,6 +116,7 @@ hipError_t hipEventCreateWithFlags(hipEvent_t *event, unsigned) {
 }
 
 hipError_t hipEventDestroy(hipEvent_t event) {
+  MockBookkeeping bookkeeping;
   check_event(event);
   g_events.erase(event);
   std::free(event);
@@ -126,6 +156,7 @@ struct hipGraphExec {
 namespace {
 hipError_t add_logged(hipGraphNode_t *node, hipGraph_t g, const hipGraphNode_t *deps, size_t n_deps, int kind,
                       uint64_t n) {
+  MockBookkeeping bookkeeping;
   if (!node || !g) die("graph node: NULL node slot or graph");
   if (n_deps && !deps) die("graph node: NULL dependencies");
   if (g_node_calls++ == g_fail_node_at) return hipErrorInvalidValue;
@@ -155,6 +186,7 @@ hipError_t add_node_for_test(hipGraphNode_t *node, hipGraph_t g, const hipGraphN
 extern "C" {
 
 hipError_t hipGraphCreate(hipGraph_t *graph, unsigned) {
+  MockBookkeeping bookkeeping;
   if (!graph) die("graph create: NULL slot");
   *graph = new ihipGraph;
   ++mock::g_live_graphs;
@@ -162,6 +194,7 @@ hipError_t hipGraphCreate(hipGraph_t *graph, unsigned) {
 }
 
 hipError_t hipGraphDestroy(hipGraph_t graph) {
+  MockBookkeeping bookkeeping;
   if (!graph) die("graph destroy: NULL");
   for (hipGraphNode *n : graph->nodes) delete n;
   delete graph;
@@ -187,6 +220,7 @@ hipError_t hipGraphAddKernelNode(hipGraphNode_t *, hipGraph_t, const hipGraphNod
 }
 
 hipError_t hipGraphInstantiateWithFlags(hipGraphExec_t *exec, hipGraph_t graph, unsigned long long) {
+  MockBookkeeping bookkeeping;
   if (!exec || !graph) die("instantiate: NULL");
   if (g_fail_instantiate) return hipErrorInvalidValue;
   *exec = new hipGraphExec{graph->log};
@@ -202,6 +236,7 @@ hipError_t hipGraphLaunch(hipGraphExec_t exec, hipStream_t) {
 }
 
 hipError_t hipGraphExecDestroy(hipGraphExec_t exec) {
+  MockBookkeeping bookkeeping;
   if (!exec) die("graph exec destroy: NULL");
   delete exec;
   --mock::g_live_execs;

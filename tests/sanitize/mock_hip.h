@@ -30,4 +30,6 @@ extern std::vector<GraphNodeLog> g_last_graph;
 extern long g_live_graphs, g_live_execs, g_graph_launches;
 void fail_graph_node_at(int k);     // the k-th node added from now fails
 void fail_instantiate(bool on);
+void fail_new_after(long k);       // the host allocation k allocations from now throws (-1: none)
+bool new_failure_pending();        // set and not yet thrown
 }  // namespace mock
