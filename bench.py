@@ -648,11 +648,12 @@ def cpu_baseline(w, budget_s=12.0):
 # hipDeviceAttribute_t values (ROCm 7.x hip_runtime_api.h): peak core clock,
 # peak memory clock (both kHz) and compute-unit count.  The unit count is
 # compared with torch's to confirm the numbering before the clocks are used.
-_ATTR_CLOCK, _ATTR_MEM_CLOCK, _ATTR_CUS = 5, 60, 63
+_ATTR_CLOCK, _ATTR_BUS_WIDTH, _ATTR_MEM_CLOCK, _ATTR_CUS = 5, 59, 60, 63
 
 
 def device_info():
-    """Name, architecture, compute units, memory and peak clocks of cuda:0."""
+    """Name, architecture, compute units, memory, peak clocks and memory bus
+    width of cuda:0."""
     import ctypes
 
     import torch
@@ -660,7 +661,7 @@ def device_info():
     p = torch.cuda.get_device_properties(0)
     info = {"name": p.name, "arch": getattr(p, "gcnArchName", None), "compute_units": p.multi_processor_count,
             "memory_GiB": round(p.total_memory / 2**30, 1), "l2_bytes": getattr(p, "L2_cache_size", None),
-            "peak_clock_MHz": None, "peak_memory_clock_MHz": None}
+            "peak_clock_MHz": None, "peak_memory_clock_MHz": None, "memory_bus_bits": None}
     try:
         hip = ctypes.CDLL("libamdhip64.so")
         v = ctypes.c_int(0)
@@ -672,6 +673,7 @@ def device_info():
             clk, mem = attr(_ATTR_CLOCK), attr(_ATTR_MEM_CLOCK)
             info["peak_clock_MHz"] = clk // 1000 if clk else None
             info["peak_memory_clock_MHz"] = mem // 1000 if mem else None
+            info["memory_bus_bits"] = attr(_ATTR_BUS_WIDTH)
     except OSError:
         pass
     return info

@@ -11,7 +11,7 @@ import torch
 import bf16_wire_all_amd as x
 import datagen as dg
 import oracle
-from tests.gpu_util import DEV, down, say, up, zeros
+from tests.gpu_util import DEV, down, filled, say, up, zeros
 
 pytestmark = pytest.mark.gpu
 
@@ -172,6 +172,42 @@ def test_graph_small_chunks_repeated_launches(R, mode):
         assert np.array_equal(down(keep[k], dt), _want(a, b, mode)), k
     assert np.array_equal(down(outs[0], dt), down(outs[1], dt))
     g.close()
+
+
+@pytest.mark.parametrize("use_graph", [False, True])
+def test_more_slots_than_chunks(use_graph):
+    """Six slots per rank and four chunks (the last one ragged): each chunk
+    takes slot c, the results match the oracle, and ring slots 4 and 5 are
+    never written (their sentinel bytes survive)."""
+    n, chunk, R = 3 * 32 + 13, 64, 6
+    a = dg.normal_f32(n, 71, 1.0)
+    b = dg.normal_f32(n, 72, 1.0)
+    send = [filled(R * chunk, 0xC3) for _ in range(2)]
+    recv = [filled(R * chunk, 0x3C) for _ in range(2)]
+    outs = [zeros(n * 4) for _ in range(2)]
+    da, db = up(a), up(b)
+    say("streamed more slots than chunks, graph", use_graph)
+    if use_graph:
+        g = x.AllReduce2Graph((da, db), send, recv, outs, chunk, x.OUT_F32)
+        g.launch()
+        torch.cuda.synchronize()
+        g.close()
+    else:
+        compute = [torch.cuda.Stream() for _ in range(2)]
+        wire = [torch.cuda.Stream() for _ in range(2)]
+        for s_ in compute + wire:
+            s_.wait_stream(torch.cuda.current_stream())
+        ev = x.Events(6 * R)
+        st = x.allreduce2_streamed((da, db), send, recv, outs, chunk, x.OUT_F32, compute, wire, ev)
+        assert st == x.OK, x.status_str(st)
+        torch.cuda.synchronize()
+        ev.close()
+    want = _want(a, b, x.OUT_F32)
+    assert np.array_equal(down(outs[0], np.uint32), want)
+    assert np.array_equal(down(outs[1], np.uint32), want)
+    for r in range(2):
+        assert (down(send[r])[4 * chunk:] == 0xC3).all()
+        assert (down(recv[r])[4 * chunk:] == 0x3C).all()
 
 
 def test_graph_prompt_batch_2048x5120():
