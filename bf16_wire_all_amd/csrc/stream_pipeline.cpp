@@ -154,15 +154,16 @@ int xfer_allreduce2_graph_deps(uint32_t n_chunks, uint32_t R, uint32_t *from, ui
     size_t k = 0;
     bool room = true;
     for_each_op_deps(n_chunks, R, [&](const xfer_op &, uint64_t i, const uint64_t *deps, uint32_t nd) {
-                       for (uint32_t j = 0; j < nd; ++j, ++k)
-                         if (k < cap && from && to) {
-                           from[k] = (uint32_t)deps[j];
-                           to[k] = (uint32_t)i;
-                         } else if (k >= cap) {
-                           room = false;
-                         }
-                       return true;
-                     });
+      for (uint32_t j = 0; j < nd; ++j, ++k) {
+        if (k >= cap) {
+          room = false;
+        } else if (from && to) {
+          from[k] = (uint32_t)deps[j];
+          to[k] = (uint32_t)i;
+        }
+      }
+      return true;
+    });
     *n_deps = k;
     if (!room) return XFER_E_RANGE;
     if (k && (!from || !to)) return XFER_E_INVAL;
@@ -355,13 +356,13 @@ int xfer_allreduce2_graph_create(const xfer_allreduce2_desc *d, hipGraphExec_t *
     if (hipGraphCreate(&owned.g, 0) != hipSuccess) return XFER_E_DEVICE;
     hipGraph_t g = owned.g;
     hipError_t err = hipSuccess;
-    for_each_op_deps((uint32_t)c.n_chunks, (uint32_t)c.R,
-                     [&](const xfer_op &op, uint64_t i, const uint64_t *deps, uint32_t nd) {
-                       hipGraphNode_t dn[3];
-                       for (uint32_t j = 0; j < nd; ++j) dn[j] = nodes[deps[j]];
-                       err = add_op_node(g, dn, nd, &nodes[i], d, c, op);
-                       return err == hipSuccess;
-                     });
+    auto add = [&](const xfer_op &op, uint64_t i, const uint64_t *deps, uint32_t nd) {
+      hipGraphNode_t dn[3];  // a stream predecessor and at most two event waits
+      for (uint32_t j = 0; j < nd; ++j) dn[j] = nodes[deps[j]];
+      err = add_op_node(g, dn, nd, &nodes[i], d, c, op);
+      return err == hipSuccess;
+    };
+    for_each_op_deps((uint32_t)c.n_chunks, (uint32_t)c.R, add);
     hipGraphExec_t e = nullptr;
     if (err == hipSuccess) err = hipGraphInstantiateWithFlags(&e, g, 0);
     if (err != hipSuccess) return XFER_E_DEVICE;  // the executable graph keeps what it needs of g
