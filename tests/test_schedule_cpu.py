@@ -210,6 +210,19 @@ def test_graph_dependencies_are_the_streams_orderings(R, n_chunks):
     assert _hazards(ops, _closure(preds)) == []
 
 
+@pytest.mark.parametrize("R,n_chunks", [(2, 40), (5, 23), (8, 8), (8, 3), (3, 31)])
+def test_graph_dependencies_larger_calls(R, n_chunks):
+    """The same equality and hazard check on longer calls: the prompt batch's
+    40 chunks through two slots, and slot counts near and above the chunk
+    count."""
+    ops = x.allreduce2_schedule(n_chunks, R)
+    preds = [set() for _ in ops]
+    for a, b in x.allreduce2_graph_deps(n_chunks, R):
+        preds[b].add(a)
+    assert preds == _direct_preds(ops)
+    assert _hazards(ops, _closure(preds)) == []
+
+
 def test_graph_dependency_edges_are_load_bearing():
     """With one slot, dropping any graph edge that stands for an event wait
     lets two conflicting operations run unordered (stream-order edges may be
