@@ -210,6 +210,32 @@ def test_more_slots_than_chunks(use_graph):
         assert (down(recv[r])[4 * chunk:] == 0x3C).all()
 
 
+def test_graph_on_a_side_stream_bf16_four_slots():
+    """The graph launched on a stream other than the current one, which waits
+    for the inputs first: 512 x 5120 through four 512 KiB slots per rank,
+    BF16 out, two launches with new inputs in between."""
+    n, chunk, R = 512 * 5120, 512 * 1024, 4
+    send = [zeros(R * chunk) for _ in range(2)]
+    recv = [zeros(R * chunk) for _ in range(2)]
+    outs = [zeros(2 * n) for _ in range(2)]
+    da, db = zeros(4 * n), zeros(4 * n)
+    g = x.AllReduce2Graph((da, db), send, recv, outs, chunk, x.OUT_BF16)
+    side = torch.cuda.Stream()
+    say("graph on a side stream, 512x5120, R", R)
+    for k in range(2):
+        a = dg.prompt_partial(n, dg.seed_for(2, 0, 512) + 7 * k)
+        b = dg.prompt_partial(n, dg.seed_for(2, 1, 512) + 7 * k)
+        da.copy_(up(a))
+        db.copy_(up(b))
+        side.wait_stream(torch.cuda.current_stream())
+        g.launch(side)
+        torch.cuda.current_stream().wait_stream(side)
+        want = _want(a, b, x.OUT_BF16)
+        assert np.array_equal(down(outs[0], np.uint16), want), k
+        assert np.array_equal(down(outs[1], np.uint16), want), k
+    g.close()
+
+
 def test_graph_prompt_batch_2048x5120():
     n, chunk, R = 2048 * 5120, 512 * 1024, 2
     a = dg.prompt_partial(n, dg.seed_for(2, 0, 2048))
