@@ -455,9 +455,12 @@ def torch_uint8():
     return torch.uint8
 
 
-def isolated_cold(w, reps=20):
-    """Each kernel of the workload on its own, cold, two ways, each kept as
-    the median of `reps` event-timed repetitions:
+WARM_SPIN_CYCLES = 200_000  # about 0.1 ms of GPU clock
+
+
+def isolated(w, reps=20):
+    """Each kernel of the workload on its own, cold two ways and warm, each
+    kept as the median of `reps` event-timed repetitions:
       after_write:      before every repetition a 1 GiB scratch buffer is
                         written with ordinary stores (more than the 256 MB
                         Infinity Cache); the cache is then full of dirty
@@ -466,6 +469,9 @@ def isolated_cold(w, reps=20):
                         (summed), which evicts those dirty lines first, so
                         the kernel starts on a cache full of clean,
                         unrelated data.
+      warm:             no flush: the repetitions follow one another, so a
+                        kernel whose bytes fit the 256 MB Infinity Cache may
+                        find its inputs there (labelled, never the headline).
     In the step, by contrast, a short kernel that follows the gather or
     scatter shares HBM with their draining writes.
 
@@ -500,14 +506,20 @@ def isolated_cold(w, reps=20):
         calls.append((f"ceiling_lib_copy@{name}", lambda p=plan, d=dst: x.copy_descs(p, d)))
         ab[f"ceiling_runtime_copy@{name}"] = ab[f"ceiling_lib_copy@{name}"] = 2 * half
         w._ceiling_keep = getattr(w, "_ceiling_keep", []) + [src, dst, buf]
-    out = {"after_write": {}, "after_write_read": {}}
+    out = {"after_write": {}, "after_write_read": {}, "warm": {}}
     for mode in out:
         for name, k in calls:
             for _ in range(3):
                 k()
             times = []
             for r in range(reps):
-                scratch.fill_(r & 0xFF)
+                if mode != "warm":
+                    scratch.fill_(r & 0xFF)
+                else:
+                    # keep the GPU busy while the events and the kernel are
+                    # enqueued, as the flush does in the cold states, so the
+                    # host's launch latency stays outside the events
+                    torch.cuda._sleep(WARM_SPIN_CYCLES)
                 if mode == "after_write_read":
                     other.sum()
                 e0, e1 = _events()
@@ -785,7 +797,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy", action="store_true", help="run only the copy used to scale PMC readings")
     ap.add_argument("--isolated", action="store_true",
-                    help="also time each kernel alone and cold (1 GiB written between repetitions)")
+                    help="also time each kernel alone: cold (1 GiB written between repetitions, then also "
+                         "read) and, labelled, warm")
     ap.add_argument("--seed-offset", type=int, default=0, help="added to every input seed (default 0)")
     ap.add_argument("--slots", type=int, default=2, help="ring slots of the streamed all-reduce (default 2)")
     ap.add_argument("--chunk-kib", type=int, default=CHUNK // 1024,
@@ -887,8 +900,8 @@ def main():
         "cpu_baseline": baseline,
     }
     if args.isolated:
-        log("bench: isolated cold pass")
-        line["isolated_cold"] = isolated_cold(w)
+        log("bench: isolated pass (cold, then warm)")
+        line["isolated"] = isolated(w)
     print(json.dumps(line), flush=True)
 
 
