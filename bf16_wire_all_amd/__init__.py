@@ -94,7 +94,8 @@ class RunsPlan(ctypes.Structure):
                 ("tile_blocks", ctypes.c_uint32), ("n_tiles", ctypes.c_uint32), ("group_blocks", ctypes.c_uint32),
                 ("n_groups", ctypes.c_uint32), ("pieces", ctypes.c_uint32), ("magic", ctypes.c_uint32),
                 ("lanes_per_wg", ctypes.c_uint32), ("off_group_run", ctypes.c_uint64), ("off_run_start", ctypes.c_uint64),
-                ("off_run_base", ctypes.c_uint64), ("off_run_stride", ctypes.c_uint64)]
+                ("off_run_base", ctypes.c_uint64), ("off_run_stride", ctypes.c_uint64), ("n_spans", ctypes.c_uint32),
+                ("reserved", ctypes.c_uint32), ("spans", ctypes.c_uint64 * 8)]
 
 
 _lib = None

@@ -99,7 +99,7 @@ Layout layout_for(const xfer_run_table *t) {
 // The checks of xfer_runs_validate; on success also reports the byte span
 // covering every segment.
 int xfer::validate_table(const xfer_run_table *t, const xfer_region *regions, int n_regions, int is_dst,
-                         uint64_t *span_lo, uint64_t *span_hi) {
+                         uint64_t *span_lo, uint64_t *span_hi, std::vector<Span> *region_spans) {
   if (!t) return XFER_E_INVAL;
   if (n_regions < 0 || (n_regions > 0 && !regions)) return XFER_E_INVAL;
   if (t->n_lanes > 0 && !t->runs_per_lane) return XFER_E_INVAL;
@@ -126,6 +126,8 @@ int xfer::validate_table(const xfer_run_table *t, const xfer_region *regions, in
   }
 
   uint64_t lo_all = UINT64_MAX, hi_all = 0;
+  std::vector<Span> per_region;
+  if (region_spans) per_region.assign((size_t)n_regions, Span{UINT64_MAX, 0});
   for (uint64_t i = 0; i < t->n_runs; ++i) {
     const uint64_t base = t->run_base[i];
     const uint32_t count = t->run_count[i];
@@ -137,12 +139,15 @@ int xfer::validate_table(const xfer_run_table *t, const xfer_region *regions, in
     const uint64_t top = std::max(base, last);
     if (top > UINT64_MAX - t->seg_bytes) return XFER_E_RANGE;
     const uint64_t hi = top + t->seg_bytes;
-    bool inside = false;
-    for (int g = 0; g < n_regions && !inside; ++g)
-      inside = lo >= regions[g].base && hi <= regions[g].base + regions[g].bytes;
-    if (!inside) return XFER_E_RANGE;
+    int g = 0;
+    while (g < n_regions && !(lo >= regions[g].base && hi <= regions[g].base + regions[g].bytes)) ++g;
+    if (g == n_regions) return XFER_E_RANGE;
     lo_all = std::min(lo_all, lo);
     hi_all = std::max(hi_all, hi);
+    if (region_spans) {
+      per_region[g].lo = std::min(per_region[g].lo, lo);
+      per_region[g].hi = std::max(per_region[g].hi, hi);
+    }
   }
 
   if (is_dst && t->n_runs) {
@@ -164,6 +169,11 @@ int xfer::validate_table(const xfer_run_table *t, const xfer_region *regions, in
   }
   if (span_lo) *span_lo = t->n_runs ? lo_all : 0;
   if (span_hi) *span_hi = t->n_runs ? hi_all : 0;
+  if (region_spans) {
+    region_spans->clear();
+    for (const Span &sp : per_region)
+      if (sp.hi > sp.lo) region_spans->push_back(sp);
+  }
   return XFER_OK;
 }
 
@@ -180,6 +190,9 @@ bool plan_ok(const xfer_runs_plan *p) {
   if (p->pieces > 1 && (p->seg_bytes / 16 / p->pieces) % 256) return false;
   if (p->lanes_per_wg == 0 || p->lanes_per_wg > xfer::kMaxLanesPerWorkgroup) return false;
   if (p->off_run_stride + up16(p->n_runs * 8) > p->dev_bytes) return false;
+  if (p->n_spans > xfer::kPlanSpans || (p->n_runs && p->n_spans == 0)) return false;
+  for (uint32_t i = 0; i < p->n_spans; ++i)
+    if (p->spans[2 * i + 1] <= p->spans[2 * i]) return false;
   return true;
 }
 
@@ -211,8 +224,31 @@ int staging_check(const xfer_runs_plan *p, uintptr_t staging, size_t staging_byt
   uint64_t need;
   if (!mul_ok((uint64_t)p->n_lanes * p->n_blocks, p->seg_bytes, &need)) return XFER_E_INVAL;
   if (!staging || !aligned16((const void *)staging) || staging_bytes < need) return XFER_E_INVAL;
-  if (overlaps(staging, need, p->span_lo, p->span_hi - p->span_lo)) return XFER_E_INVAL;
+  for (uint32_t i = 0; i < p->n_spans; ++i)
+    if (overlaps(staging, need, p->spans[2 * i], p->spans[2 * i + 1] - p->spans[2 * i])) return XFER_E_INVAL;
   return XFER_OK;
+}
+
+// At most kPlanSpans ranges, sorted, overlapping or touching ones joined; while
+// there are more, the two with the smallest gap between them are joined (the
+// result still covers every segment).
+std::vector<xfer::Span> fold_spans(std::vector<xfer::Span> v) {
+  std::sort(v.begin(), v.end(), [](const xfer::Span &a, const xfer::Span &b) { return a.lo < b.lo; });
+  std::vector<xfer::Span> out;
+  for (const xfer::Span &sp : v) {
+    if (!out.empty() && sp.lo <= out.back().hi)
+      out.back().hi = std::max(out.back().hi, sp.hi);
+    else
+      out.push_back(sp);
+  }
+  while (out.size() > xfer::kPlanSpans) {
+    size_t best = 0;
+    for (size_t i = 1; i + 1 < out.size(); ++i)
+      if (out[i + 1].lo - out[i].hi < out[best + 1].lo - out[best].hi) best = i;
+    out[best].hi = out[best + 1].hi;
+    out.erase(out.begin() + (std::ptrdiff_t)best + 1);
+  }
+  return out;
 }
 
 }  // namespace
@@ -431,7 +467,7 @@ int xfer_runs_encode(const uint64_t *addrs, uint32_t n_lanes, uint32_t n_blocks,
 
 int xfer_runs_validate(const xfer_run_table *t, const xfer_region *regions, int n_regions, int is_dst) {
   return xfer::guarded([&]() -> int {
-    return validate_table(t, regions, n_regions, is_dst, nullptr, nullptr);
+    return validate_table(t, regions, n_regions, is_dst, nullptr, nullptr, nullptr);
   });
 }
 
@@ -444,7 +480,8 @@ int xfer_runs_prepare(const xfer_run_table *t, const xfer_region *regions, int n
                       size_t dev_bytes, xfer_runs_plan *out) {
   return xfer::guarded([&]() -> int {
     uint64_t span_lo = 0, span_hi = 0;
-    const int st = validate_table(t, regions, n_regions, is_dst, &span_lo, &span_hi);
+    std::vector<xfer::Span> region_spans;
+    const int st = validate_table(t, regions, n_regions, is_dst, &span_lo, &span_hi, &region_spans);
     if (st != XFER_OK) return st;
     if (!out) return XFER_E_INVAL;
     const Layout L = layout_for(t);
@@ -487,6 +524,12 @@ int xfer_runs_prepare(const xfer_run_table *t, const xfer_region *regions, int n
     p.n_runs = t->n_runs;
     p.span_lo = span_lo;
     p.span_hi = span_hi;
+    const std::vector<xfer::Span> spans = fold_spans(region_spans);
+    p.n_spans = (uint32_t)spans.size();
+    for (size_t i = 0; i < spans.size(); ++i) {
+      p.spans[2 * i] = spans[i].lo;
+      p.spans[2 * i + 1] = spans[i].hi;
+    }
     p.is_dst = is_dst ? 1u : 0u;
     p.tile_blocks = L.tile_blocks;
     p.n_tiles = L.n_tiles;

@@ -37,7 +37,7 @@ int xfer_groups_plan(const xfer_run_table *t, const xfer_region *regions, int n_
                      xfer_desc *descs, uint64_t cap_descs, uint64_t *n_descs, uint64_t *slab_bytes,
                      uint64_t *local_base, int64_t *local_stride, uint64_t *n_groups, uint64_t *n_dense) {
   return xfer::guarded([&]() -> int {
-    const int st = xfer::validate_table(t, regions, n_regions, 0, nullptr, nullptr);
+    const int st = xfer::validate_table(t, regions, n_regions, 0, nullptr, nullptr, nullptr);
     if (st != XFER_OK) return st;
     if (!n_descs || !slab_bytes || max_desc_bytes == 0 || max_desc_bytes % 16) return XFER_E_INVAL;
     if (t->n_runs && (!local_base || !local_stride)) return XFER_E_INVAL;

@@ -8,6 +8,7 @@
 #include <new>
 #include <stdexcept>
 #include <type_traits>
+#include <vector>
 
 #include "xfer.h"
 
@@ -75,8 +76,15 @@ struct PagesView {
 hipError_t launch_paged_copy(const PagesView &v, hipStream_t stream);
 
 // ---- host helpers shared by the entry points (api.cpp)
+// Per declared region that holds segments, the [lo, hi) byte range of those
+// segments (filled in region order when region_spans is not NULL).
+struct Span {
+  uint64_t lo, hi;
+};
 int validate_table(const xfer_run_table *t, const xfer_region *regions, int n_regions, int is_dst,
-                   uint64_t *span_lo, uint64_t *span_hi);
+                   uint64_t *span_lo, uint64_t *span_hi, std::vector<Span> *region_spans);
+// A plan keeps at most this many segment spans (xfer_runs_plan::spans).
+constexpr uint32_t kPlanSpans = 4;
 bool run_addr(uint64_t base, int64_t stride, uint64_t k, uint64_t *out);
 
 // ---- pack / combine (pack_combine.hip)

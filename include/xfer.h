@@ -324,6 +324,8 @@ typedef struct {
   uint32_t magic;
   uint32_t lanes_per_wg;
   uint64_t off_group_run, off_run_start, off_run_base, off_run_stride;
+  uint32_t n_spans, reserved;
+  uint64_t spans[8];         /* up to 4 [lo, hi) pairs, see xfer_gather_runs */
 } xfer_runs_plan;
 
 /* Device bytes xfer_runs_prepare needs for table t (0 if t is NULL). */
@@ -350,7 +352,12 @@ XFER_API int xfer_runs_prepare(const xfer_run_table *t, const xfer_region *regio
  * inside a block.
  *
  *   staging  (device) at least n_lanes * n_blocks * seg_bytes bytes,
- *            16-byte aligned, not overlapping [span_lo, span_hi).
+ *            16-byte aligned, and sharing no byte with the plan's segment
+ *            spans: per declared region that holds segments, the range from
+ *            its lowest to its highest segment byte.  A plan keeps at most
+ *            four such ranges; beyond four, the two nearest are merged until
+ *            four remain (so a buffer between two far-apart regions is
+ *            accepted, one inside a region's segment range is not).
  * Errors: XFER_E_INVAL for a NULL / foreign / destination plan, a small,
  * misaligned or overlapping staging buffer.
  */

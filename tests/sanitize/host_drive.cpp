@@ -482,6 +482,65 @@ void streamed(Rng &g) {
 }
 
 // A launch the runtime refuses comes back as XFER_E_DEVICE from every hot call.
+// Staging checked against per-region segment spans: a buffer between two
+// regions is accepted; one inside a region's segment range, or inside a gap
+// that was merged away to keep four spans, is refused.  Six one-segment
+// regions at offsets 0, 7, 20, 27, 60 and 67 segments; staging is six
+// segments long.  The two smallest gaps ([1, 7) and [21, 27)) are merged.
+void staging_spans() {
+  const uint64_t U = 4096;
+  const uint64_t off[6] = {0, 7, 20, 27, 60, 67};
+  Buf arena(70 * U);
+  const uint64_t a0 = arena.addr();
+  std::vector<uint32_t> rpl(6, 1), cnt(6, 1);
+  std::vector<uint64_t> base(6);
+  std::vector<int64_t> stride(6, 0);
+  std::vector<xfer_region> regs(6);
+  for (int i = 0; i < 6; ++i) {
+    base[i] = a0 + off[i] * U;
+    regs[i] = xfer_region{base[i], U};
+  }
+  xfer_run_table t{6, 1, U, 6, rpl.data(), base.data(), stride.data(), cnt.data()};
+  Buf dev(xfer_runs_plan_bytes(&t));
+  for (int is_dst = 0; is_dst < 2; ++is_dst) {
+    xfer_runs_plan p;
+    CHECK(xfer_runs_prepare(&t, regs.data(), 6, is_dst, dev.p, dev.n, &p) == XFER_OK);
+    CHECK(p.n_spans == 4);
+    CHECK(p.spans[0] == a0 && p.spans[1] == a0 + 8 * U);            // [0, 8): the first gap merged
+    CHECK(p.spans[2] == a0 + 20 * U && p.spans[3] == a0 + 28 * U);  // [20, 28): the third gap merged
+    CHECK(p.spans[4] == a0 + 60 * U && p.spans[5] == a0 + 61 * U);
+    CHECK(p.spans[6] == a0 + 67 * U && p.spans[7] == a0 + 68 * U);
+    const struct {
+      uint64_t at;
+      int want;
+    } cases[] = {{1, XFER_E_INVAL}, {8, XFER_OK}, {14, XFER_OK}, {15, XFER_E_INVAL}, {21, XFER_E_INVAL},
+                 {28, XFER_OK}, {54, XFER_OK}, {55, XFER_E_INVAL}, {61, XFER_OK}, {62, XFER_E_INVAL}};
+    for (const auto &c : cases) {
+      uint8_t *stg = arena.p + c.at * U;
+      const int st = is_dst ? xfer_scatter_runs(stg, 6 * U, &p, token(9)) : xfer_gather_runs(&p, stg, 6 * U, token(9));
+      CHECK(st == c.want);
+    }
+    // an edited plan with no spans for its segments, or a reversed span, is refused
+    xfer_runs_plan bad = p;
+    bad.n_spans = 0;
+    CHECK(xfer_gather_runs(&bad, arena.p + 8 * U, 6 * U, token(9)) == XFER_E_INVAL);
+    bad = p;
+    bad.n_spans = 5;
+    CHECK(xfer_gather_runs(&bad, arena.p + 8 * U, 6 * U, token(9)) == XFER_E_INVAL);
+    bad = p;
+    std::swap(bad.spans[0], bad.spans[1]);
+    CHECK(xfer_gather_runs(&bad, arena.p + 8 * U, 6 * U, token(9)) == XFER_E_INVAL);
+  }
+  // two regions: the whole range between them is free for staging
+  xfer_run_table t2{2, 1, U, 2, rpl.data(), base.data(), stride.data(), cnt.data()};
+  Buf dev2(xfer_runs_plan_bytes(&t2));
+  xfer_runs_plan p2;
+  CHECK(xfer_runs_prepare(&t2, regs.data(), 6, 0, dev2.p, dev2.n, &p2) == XFER_OK);
+  CHECK(p2.n_spans == 2 && p2.span_lo == a0 && p2.span_hi == a0 + 8 * U);
+  CHECK(xfer_gather_runs(&p2, arena.p + 1 * U, 2 * U, token(9)) == XFER_OK);
+  CHECK(xfer_gather_runs(&p2, arena.p + 6 * U, 2 * U, token(9)) == XFER_E_INVAL);
+}
+
 void refused_launches() {
   const size_t n = 1000;
   Buf src(n * 4), ring(2 * 64), a(n * 2), b(n * 2), out(n * 4);
@@ -566,6 +625,7 @@ int main() {
   Rng g{0x5EED5A5Eull};
   statuses();
   pack_combine(g);
+  staging_spans();
   argmax(g);
   runs_and_groups(g);
   pages(g);

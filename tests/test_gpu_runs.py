@@ -262,3 +262,47 @@ def test_odd_lane_count_scattered_table():
     mwant = np.full(mirror.numel(), 0x5A, np.uint8)
     oracle.scatter(_otable(mt), seg, [(mirror.data_ptr(), mwant)], want)
     assert np.array_equal(down(mirror), mwant)
+
+
+def test_staging_between_the_two_regions():
+    """One allocation holds region 0, then the staging buffer, then region 1:
+    the staging shares no byte with either region's segments, so the gather
+    into it and the scatter out of it (into a second allocation laid out the
+    same way) are accepted and match the oracle; a staging buffer that runs
+    one segment into region 1 is refused."""
+    n_blocks, n_slots, seg = 40, 6, 4096
+    rb = dg.region_bytes_for(n_blocks, n_slots, seg, 2)
+    sb = 2 * n_slots * n_blocks * seg                          # = 2 * rb
+    arena = zeros(rb + sb + rb)
+    bases = [arena.data_ptr(), arena.data_ptr() + rb + sb]
+    addrs = dg.kv_src_addrs(n_blocks, n_slots, seg, bases, pos=dg.permutation(n_blocks, 77))
+    hosts = []
+    for i in range(2):
+        h = np.empty(rb, np.uint8)
+        dg.fill_region(h, bases[i], addrs, seg, 2000 + i)
+        hosts.append(h)
+    arena[:rb].copy_(torch.from_numpy(hosts[0]))
+    arena[rb + sb:].copy_(torch.from_numpy(hosts[1]))
+    t = x.runs_encode(addrs, seg)
+    plan, _b = _plan(t, [(bases[0], rb), (bases[1], rb)], False)
+    assert plan.n_spans == 2
+    staging = arena[rb:rb + sb]
+    say("staging between the regions", n_blocks, n_slots)
+    assert x.gather_runs_raw(plan, staging.data_ptr() + seg, sb) == x.E_INVAL     # one segment into region 1
+    x.gather_runs(plan, staging)
+    want = oracle.gather(_otable(t), seg, [(bases[0], hosts[0]), (bases[1], hosts[1])])
+    assert np.array_equal(down(staging), want)
+    assert np.array_equal(down(arena[:rb]), hosts[0]) and np.array_equal(down(arena[rb + sb:]), hosts[1])
+    # scatter from a staging buffer between the two destination regions
+    arena2 = filled(rb + sb + rb, 0x5A)
+    dbases = [arena2.data_ptr(), arena2.data_ptr() + rb + sb]
+    daddrs = dg.kv_src_addrs(n_blocks, n_slots, seg, dbases)
+    dt = x.runs_encode(daddrs, seg)
+    dplan, _db = _plan(dt, [(dbases[0], rb), (dbases[1], rb)], True)
+    stg2 = arena2[rb:rb + sb]
+    stg2.copy_(up(want))
+    x.scatter_runs(stg2, dplan)
+    dwant = [np.full(rb, 0x5A, np.uint8) for _ in range(2)]
+    oracle.scatter(_otable(dt), seg, [(dbases[0], dwant[0]), (dbases[1], dwant[1])], want)
+    assert np.array_equal(down(arena2[:rb]), dwant[0]) and np.array_equal(down(arena2[rb + sb:]), dwant[1])
+    assert np.array_equal(down(stg2), want)
