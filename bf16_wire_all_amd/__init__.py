@@ -69,7 +69,8 @@ class DescsPlan(ctypes.Structure):
     _fields_ = [("dev", ctypes.c_void_p), ("dev_bytes", ctypes.c_uint64), ("n_descs", ctypes.c_uint64),
                 ("slab_bytes", ctypes.c_uint64), ("src_lo", ctypes.c_uint64), ("src_hi", ctypes.c_uint64),
                 ("max_pieces", ctypes.c_uint32), ("piece_bytes", ctypes.c_uint32), ("magic", ctypes.c_uint32),
-                ("reserved", ctypes.c_uint32)]
+                ("reserved", ctypes.c_uint32), ("n_spans", ctypes.c_uint32), ("reserved2", ctypes.c_uint32),
+                ("spans", ctypes.c_uint64 * 8)]
 
 
 class PagesC(ctypes.Structure):

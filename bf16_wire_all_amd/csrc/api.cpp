@@ -190,10 +190,7 @@ bool plan_ok(const xfer_runs_plan *p) {
   if (p->pieces > 1 && (p->seg_bytes / 16 / p->pieces) % 256) return false;
   if (p->lanes_per_wg == 0 || p->lanes_per_wg > xfer::kMaxLanesPerWorkgroup) return false;
   if (p->off_run_stride + up16(p->n_runs * 8) > p->dev_bytes) return false;
-  if (p->n_spans > xfer::kPlanSpans || (p->n_runs && p->n_spans == 0)) return false;
-  for (uint32_t i = 0; i < p->n_spans; ++i)
-    if (p->spans[2 * i + 1] <= p->spans[2 * i]) return false;
-  return true;
+  return xfer::spans_ok(p->spans, p->n_spans, p->n_runs != 0);
 }
 
 PlanView view_of(const xfer_runs_plan *p) {
@@ -224,15 +221,13 @@ int staging_check(const xfer_runs_plan *p, uintptr_t staging, size_t staging_byt
   uint64_t need;
   if (!mul_ok((uint64_t)p->n_lanes * p->n_blocks, p->seg_bytes, &need)) return XFER_E_INVAL;
   if (!staging || !aligned16((const void *)staging) || staging_bytes < need) return XFER_E_INVAL;
-  for (uint32_t i = 0; i < p->n_spans; ++i)
-    if (overlaps(staging, need, p->spans[2 * i], p->spans[2 * i + 1] - p->spans[2 * i])) return XFER_E_INVAL;
+  if (xfer::overlaps_spans(staging, need, p->spans, p->n_spans)) return XFER_E_INVAL;
   return XFER_OK;
 }
 
-// At most kPlanSpans ranges, sorted, overlapping or touching ones joined; while
-// there are more, the two with the smallest gap between them are joined (the
-// result still covers every segment).
-std::vector<xfer::Span> fold_spans(std::vector<xfer::Span> v) {
+}  // namespace
+
+std::vector<xfer::Span> xfer::fold_spans(std::vector<Span> v) {
   std::sort(v.begin(), v.end(), [](const xfer::Span &a, const xfer::Span &b) { return a.lo < b.lo; });
   std::vector<xfer::Span> out;
   for (const xfer::Span &sp : v) {
@@ -251,7 +246,18 @@ std::vector<xfer::Span> fold_spans(std::vector<xfer::Span> v) {
   return out;
 }
 
-}  // namespace
+bool xfer::overlaps_spans(uintptr_t a, uint64_t na, const uint64_t *spans, uint32_t n) {
+  for (uint32_t i = 0; i < n; ++i)
+    if (overlaps(a, na, spans[2 * i], spans[2 * i + 1] - spans[2 * i])) return true;
+  return false;
+}
+
+bool xfer::spans_ok(const uint64_t *spans, uint32_t n, bool has_work) {
+  if (n > kPlanSpans || (has_work && n == 0)) return false;
+  for (uint32_t i = 0; i < n; ++i)
+    if (spans[2 * i + 1] <= spans[2 * i]) return false;
+  return true;
+}
 
 extern "C" {
 
@@ -524,7 +530,7 @@ int xfer_runs_prepare(const xfer_run_table *t, const xfer_region *regions, int n
     p.n_runs = t->n_runs;
     p.span_lo = span_lo;
     p.span_hi = span_hi;
-    const std::vector<xfer::Span> spans = fold_spans(region_spans);
+    const std::vector<xfer::Span> spans = xfer::fold_spans(region_spans);
     p.n_spans = (uint32_t)spans.size();
     for (size_t i = 0; i < spans.size(); ++i) {
       p.spans[2 * i] = spans[i].lo;

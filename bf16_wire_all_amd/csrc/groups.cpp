@@ -155,18 +155,21 @@ int xfer_descs_prepare(const xfer_desc *descs, uint64_t n_descs, uint64_t slab_b
       if (regions[i].base > UINT64_MAX - regions[i].bytes) return XFER_E_INVAL;
     uint64_t lo_all = UINT64_MAX, hi_all = 0;
     std::vector<std::pair<uint64_t, uint64_t>> dst(n_descs);
+    std::vector<xfer::Span> per_region((size_t)n_regions, xfer::Span{UINT64_MAX, 0});
     for (uint64_t i = 0; i < n_descs; ++i) {
       const xfer_desc &d = descs[i];
       if (d.bytes == 0 || !aligned16(d.src) || !aligned16(d.dst_off) || !aligned16(d.bytes)) return XFER_E_INVAL;
       if (d.src > UINT64_MAX - d.bytes) return XFER_E_RANGE;
-      bool inside = false;
-      for (int g = 0; g < n_regions && !inside; ++g)
-        inside = d.src >= regions[g].base && d.src + d.bytes <= regions[g].base + regions[g].bytes;
-      if (!inside) return XFER_E_RANGE;
+      int g = 0;
+      while (g < n_regions && !(d.src >= regions[g].base && d.src + d.bytes <= regions[g].base + regions[g].bytes))
+        ++g;
+      if (g == n_regions) return XFER_E_RANGE;
       if (d.dst_off > slab_bytes || slab_bytes - d.dst_off < d.bytes) return XFER_E_RANGE;
       dst[i] = {d.dst_off, d.bytes};
       lo_all = std::min(lo_all, d.src);
       hi_all = std::max(hi_all, d.src + d.bytes);
+      per_region[g].lo = std::min(per_region[g].lo, d.src);
+      per_region[g].hi = std::max(per_region[g].hi, d.src + d.bytes);
     }
     std::sort(dst.begin(), dst.end());
     for (size_t i = 1; i < dst.size(); ++i)
@@ -187,6 +190,15 @@ int xfer_descs_prepare(const xfer_desc *descs, uint64_t n_descs, uint64_t slab_b
     p.slab_bytes = slab_bytes;
     p.src_lo = n_descs ? lo_all : 0;
     p.src_hi = n_descs ? hi_all : 0;
+    std::vector<xfer::Span> used;
+    for (const xfer::Span &sp : per_region)
+      if (sp.hi > sp.lo) used.push_back(sp);
+    const std::vector<xfer::Span> spans = xfer::fold_spans(used);
+    p.n_spans = (uint32_t)spans.size();
+    for (size_t i = 0; i < spans.size(); ++i) {
+      p.spans[2 * i] = spans[i].lo;
+      p.spans[2 * i + 1] = spans[i].hi;
+    }
     p.max_pieces = (uint32_t)pieces;
     p.piece_bytes = xfer::kDescPieceBytes;
     p.magic = kDescMagic;
@@ -200,8 +212,8 @@ int xfer_copy_descs(const xfer_descs_plan *plan, void *slab, size_t slab_bytes, 
   if (plan->n_descs == 0) return XFER_OK;
   if (!plan->dev || plan->dev_bytes < plan->n_descs * sizeof(xfer_desc)) return XFER_E_INVAL;
   if (!slab || ((uintptr_t)slab & 15u) || slab_bytes < plan->slab_bytes) return XFER_E_INVAL;
-  const uintptr_t s = (uintptr_t)slab;
-  if (s < plan->src_hi && plan->src_lo < s + plan->slab_bytes) return XFER_E_INVAL;
+  if (!xfer::spans_ok(plan->spans, plan->n_spans, true)) return XFER_E_INVAL;
+  if (xfer::overlaps_spans((uintptr_t)slab, plan->slab_bytes, plan->spans, plan->n_spans)) return XFER_E_INVAL;
   if (xfer::launch_copy_descs(reinterpret_cast<const xfer_desc *>(plan->dev), plan->n_descs, plan->max_pieces, slab,
                               stream) != hipSuccess)
     return XFER_E_DEVICE;

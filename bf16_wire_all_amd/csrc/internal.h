@@ -83,8 +83,18 @@ struct Span {
 };
 int validate_table(const xfer_run_table *t, const xfer_region *regions, int n_regions, int is_dst,
                    uint64_t *span_lo, uint64_t *span_hi, std::vector<Span> *region_spans);
-// A plan keeps at most this many segment spans (xfer_runs_plan::spans).
+// A plan keeps at most this many spans (xfer_runs_plan::spans,
+// xfer_descs_plan::spans).
 constexpr uint32_t kPlanSpans = 4;
+// At most kPlanSpans ranges covering the given ones: sorted, overlapping or
+// touching ranges joined, then the two with the smallest gap joined while
+// there are more.
+std::vector<Span> fold_spans(std::vector<Span> v);
+// Whether [a, a + na) shares a byte with any of the n [lo, hi) pairs.
+bool overlaps_spans(uintptr_t a, uint64_t na, const uint64_t *spans, uint32_t n);
+// Plan-side check of a span list: at most kPlanSpans, each non-empty, and at
+// least one when the plan has work.
+bool spans_ok(const uint64_t *spans, uint32_t n, bool has_work);
 bool run_addr(uint64_t base, int64_t stride, uint64_t k, uint64_t *out);
 
 // ---- pack / combine (pack_combine.hip)

@@ -429,6 +429,8 @@ typedef struct {
   uint32_t piece_bytes;
   uint32_t magic;
   uint32_t reserved;
+  uint32_t n_spans, reserved2;
+  uint64_t spans[8];        /* up to 4 [lo, hi) pairs, see xfer_copy_descs */
 } xfer_descs_plan;
 
 XFER_API size_t xfer_descs_plan_bytes(uint64_t n_descs);
@@ -449,7 +451,10 @@ XFER_API int xfer_descs_prepare(const xfer_desc *descs, uint64_t n_descs, uint64
 /*
  * xfer_copy_descs - execute the plan: slab[dst_off + k] = *(src + k) for every
  * descriptor, k < bytes.  slab (device) is slab_bytes long at least, 16-byte
- * aligned, and must not overlap [src_lo, src_hi).
+ * aligned, and shares no byte with the plan's source spans: per declared
+ * region that holds sources, the range from its lowest to its highest source
+ * byte (at most four ranges; beyond four the two nearest are merged, as for
+ * run plans).
  */
 XFER_API int xfer_copy_descs(const xfer_descs_plan *plan, void *slab, size_t slab_bytes, hipStream_t stream);
 

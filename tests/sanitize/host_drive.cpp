@@ -482,9 +482,9 @@ void streamed(Rng &g) {
 }
 
 // A launch the runtime refuses comes back as XFER_E_DEVICE from every hot call.
-// Staging checked against per-region segment spans: a buffer between two
-// regions is accepted; one inside a region's segment range, or inside a gap
-// that was merged away to keep four spans, is refused.  Six one-segment
+// Staging (and the coalesced fetch's slab) checked against per-region spans:
+// a buffer between two regions is accepted; one inside a region's segment
+// range, or inside a gap that was merged away to keep four spans, is refused.  Six one-segment
 // regions at offsets 0, 7, 20, 27, 60 and 67 segments; staging is six
 // segments long.  The two smallest gaps ([1, 7) and [21, 27)) are merged.
 void staging_spans() {
@@ -530,6 +530,28 @@ void staging_spans() {
     bad = p;
     std::swap(bad.spans[0], bad.spans[1]);
     CHECK(xfer_gather_runs(&bad, arena.p + 8 * U, 6 * U, token(9)) == XFER_E_INVAL);
+  }
+  // the coalesced fetch's slab, checked the same way against per-region source spans
+  {
+    std::vector<xfer_desc> d(6);
+    for (int i = 0; i < 6; ++i) d[i] = xfer_desc{base[i], (uint64_t)i * U, U};
+    Buf ddev(xfer_descs_plan_bytes(6));
+    xfer_descs_plan p;
+    CHECK(xfer_descs_prepare(d.data(), 6, 6 * U, regs.data(), 6, ddev.p, ddev.n, &p) == XFER_OK);
+    CHECK(p.n_spans == 4 && p.src_lo == a0 && p.src_hi == a0 + 68 * U);
+    CHECK(p.spans[0] == a0 && p.spans[1] == a0 + 8 * U && p.spans[2] == a0 + 20 * U && p.spans[3] == a0 + 28 * U);
+    const struct {
+      uint64_t at;
+      int want;
+    } cases[] = {{1, XFER_E_INVAL}, {8, XFER_OK}, {15, XFER_E_INVAL}, {28, XFER_OK}, {61, XFER_OK},
+                 {62, XFER_E_INVAL}};
+    for (const auto &c : cases) CHECK(xfer_copy_descs(&p, arena.p + c.at * U, 6 * U, token(9)) == c.want);
+    xfer_descs_plan bad = p;
+    bad.n_spans = 0;
+    CHECK(xfer_copy_descs(&bad, arena.p + 8 * U, 6 * U, token(9)) == XFER_E_INVAL);
+    bad = p;
+    bad.spans[3] = bad.spans[2];
+    CHECK(xfer_copy_descs(&bad, arena.p + 8 * U, 6 * U, token(9)) == XFER_E_INVAL);
   }
   // two regions: the whole range between them is free for staging
   xfer_run_table t2{2, 1, U, 2, rpl.data(), base.data(), stride.data(), cnt.data()};

@@ -144,3 +144,44 @@ def test_fetch_misuse_refused():
     empty = x.descs_prepare(np.zeros(0, x.DESC), 0, region, dev)
     assert L.xfer_copy_descs(ctypes.byref(empty), slab.data_ptr(), 16, None) == x.OK
     assert np.all(down(slab) == 0x11)
+
+
+def test_slab_between_the_two_regions():
+    """One allocation holds region 0, then the slab, then region 1: the slab
+    shares no byte with either region's sources, so the fetch into it is
+    accepted and equals the oracle's copy; a slab reaching into region 1 is
+    refused."""
+    n_blocks, n_slots, seg = 30, 6, 4096
+    rb = dg.region_bytes_for(n_blocks, n_slots, seg, 2)
+    sb = 2 * rb
+    arena = zeros(rb + sb + rb)
+    bases = [arena.data_ptr(), arena.data_ptr() + rb + sb]
+    addrs = dg.kv_src_addrs(n_blocks, n_slots, seg, bases, pos=dg.permutation(n_blocks, 91))
+    hosts = []
+    for i in range(2):
+        h = np.empty(rb, np.uint8)
+        dg.fill_region(h, bases[i], addrs, seg, 4000 + i)
+        hosts.append(h)
+    arena[:rb].copy_(torch.from_numpy(hosts[0]))
+    arena[rb + sb:].copy_(torch.from_numpy(hosts[1]))
+    t = x.runs_encode(addrs, seg)
+    regions = [(bases[0], rb), (bases[1], rb)]
+    g = x.groups_plan(t, regions)
+    assert g.slab_bytes == sb
+    dev = zeros(max(16, x.descs_plan_bytes(len(g.descs))))
+    p = x.descs_prepare(g.descs, g.slab_bytes, regions, dev)
+    assert p.n_spans == 2
+    say("slab between the regions", n_blocks, n_slots)
+    assert lib_copy(p, arena.data_ptr() + rb + seg, sb) == x.E_INVAL            # one segment into region 1
+    slab = arena[rb:rb + sb]
+    x.copy_descs(p, slab)
+    want = np.zeros(sb, np.uint8)
+    oracle.copy_descs(g.descs, [(bases[0], hosts[0]), (bases[1], hosts[1])], want)
+    assert np.array_equal(down(slab), want)
+    assert np.array_equal(down(arena[:rb]), hosts[0]) and np.array_equal(down(arena[rb + sb:]), hosts[1])
+
+
+def lib_copy(plan, slab_ptr, slab_bytes):
+    """The raw call (returns the status; the current stream)."""
+    return x.lib().xfer_copy_descs(ctypes.byref(plan), slab_ptr, slab_bytes,
+                                   torch.cuda.current_stream().cuda_stream)
