@@ -369,7 +369,7 @@ int argmax_checks(const xfer_shard *s0, const xfer_shard *s1, int mode, const vo
     if (a0 < b1 && b0 < a1) return XFER_E_INVAL;
   }
   for (int i = 0; i < 2; ++i) {
-    if (s[i]->ncols > 65536) return XFER_E_UNSUPPORTED;
+    if (s[i]->ncols > xfer::kArgmaxMaxShardCols) return XFER_E_UNSUPPORTED;
     if (!s[i]->ptr || !aligned16(s[i]->ptr) || (s[i]->ld * 2) % 16) return XFER_E_INVAL;
     if (rows > 1 && s[i]->ld < s[i]->ncols) return XFER_E_INVAL;
     uint64_t last_row;

@@ -16,13 +16,16 @@
 // the counter updates of a row's workgroups serialise, and an agent-scope
 // release in every workgroup writes back L2.)
 //
-// Keys: inside a shard an element is the 32-bit key
-//     ord(value) << 16 | (0xFFFF - local column)
+// Keys: inside a slice an element is the 32-bit key
+//     ord(value) << 16 | (0xFFFF - column within the slice)
 // where ord maps BF16 bit patterns to 16-bit integers in numeric order with
 // -0 and +0 equal (0x8000 +- magnitude).  A larger key is earlier in the
-// row order (larger value, then lower id), keys are unique per shard, and 0
-// (below every finite value and -inf) marks "no element".  The first two
-// elements of any set follow from the pairwise merge
+// row order (larger value, then lower id), keys are unique per slice, and 0
+// (below every finite value and -inf) marks "no element".  A slice is at most
+// 65,536 columns wide, so a shard of up to 32 slices may hold 2,097,152.  The
+// fold widens a slice's keys to 64 bits, ord << 32 | (0xFFFFFFFF - column
+// within the shard), which orders elements of different slices the same way.
+// The first two elements of any set follow from the pairwise merge
 //     top1 = max(x1, y1), top2 = max(min(x1, y1), max(x2, y2)).
 // The wavefront reductions use DPP lane moves.
 #include <atomic>
@@ -69,7 +72,6 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
-constexpr uint32_t kMaxSplits = 32;  // 2 * splits partials fit one wavefront
 constexpr uint32_t kTargetWorkgroups = 1024;
 constexpr uint32_t kMinSliceCols = 1024;
 
@@ -91,7 +93,7 @@ __device__ __forceinline__ void merge(uint32_t &t1, uint32_t &t2, uint32_t o1, u
   t2 = n2;
 }
 
-// The 8 elements of a 16-byte vector whose first column is `col`.
+// The 8 elements of a 16-byte vector whose first column (within the slice) is `col`.
 __device__ __forceinline__ void take8(uint32_t &t1, uint32_t &t2, v4u w, uint32_t col) {
   const uint32_t id = 0xFFFFu - col;
   const uint32_t x[4] = {w.x, w.y, w.z, w.w};
@@ -119,6 +121,36 @@ __device__ __forceinline__ void wave_reduce(uint32_t &t1, uint32_t &t2) {
   dpp_merge<0x118, 0xF>(t1, t2);  // row_shr:8: lane 15 of each row holds the row
   dpp_merge<0x142, 0xA>(t1, t2);  // row_bcast:15 into rows 1 and 3
   dpp_merge<0x143, 0xC>(t1, t2);  // row_bcast:31 into rows 2 and 3: lane 63 holds all
+}
+
+// The same reduction on 64-bit keys (each DPP move is two 32-bit moves).
+__device__ __forceinline__ void merge64(uint64_t &t1, uint64_t &t2, uint64_t o1, uint64_t o2) {
+  const uint64_t n2 = max(max(t2, o2), min(t1, o1));
+  t1 = max(t1, o1);
+  t2 = n2;
+}
+
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint64_t dpp64(uint64_t v) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, ROW_MASK, 0xF, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), CTRL, ROW_MASK, 0xF, false);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ void dpp_merge64(uint64_t &t1, uint64_t &t2) {
+  const uint64_t o1 = dpp64<CTRL, ROW_MASK>(t1);
+  const uint64_t o2 = dpp64<CTRL, ROW_MASK>(t2);
+  merge64(t1, t2, o1, o2);
+}
+
+__device__ __forceinline__ void wave_reduce64(uint64_t &t1, uint64_t &t2) {
+  dpp_merge64<0xB1, 0xF>(t1, t2);
+  dpp_merge64<0x4E, 0xF>(t1, t2);
+  dpp_merge64<0x114, 0xF>(t1, t2);
+  dpp_merge64<0x118, 0xF>(t1, t2);
+  dpp_merge64<0x142, 0xA>(t1, t2);
+  dpp_merge64<0x143, 0xC>(t1, t2);
 }
 
 struct Shards {
@@ -149,18 +181,19 @@ __global__ __launch_bounds__(kThreads) void argmax_scan_kernel(Shards sh, uint32
   const uint32_t n_vec = (c1 - c0) / 8;
   const v4u *vp = reinterpret_cast<const v4u *>(rowp + c0);
   uint32_t v = tid;
+  // Columns are counted from the slice start (c1 - c0 <= 65,536).
   for (; v + kThreads < n_vec; v += 2 * kThreads) {
     const v4u w0 = __builtin_nontemporal_load(&vp[v]);
     const v4u w1 = __builtin_nontemporal_load(&vp[v + kThreads]);
-    take8(t1, t2, w0, c0 + 8 * v);
-    take8(t1, t2, w1, c0 + 8 * (v + kThreads));
+    take8(t1, t2, w0, 8 * v);
+    take8(t1, t2, w1, 8 * (v + kThreads));
   }
-  for (; v < n_vec; v += kThreads) take8(t1, t2, __builtin_nontemporal_load(&vp[v]), c0 + 8 * v);
+  for (; v < n_vec; v += kThreads) take8(t1, t2, __builtin_nontemporal_load(&vp[v]), 8 * v);
   // Columns past the last whole vector (only in a shard's last slice).
   const uint32_t c_tail = c0 + 8 * n_vec;
   if (tid < c1 - c_tail) {
     const uint32_t c = c_tail + tid;
-    take(t1, t2, (ord16(rowp[c]) << 16) | (0xFFFFu - c));
+    take(t1, t2, (ord16(rowp[c]) << 16) | (0xFFFFu - (c - c0)));
   }
 
   wave_reduce(t1, t2);
@@ -188,10 +221,20 @@ __global__ __launch_bounds__(64) void argmax_fold_kernel(Shards sh, uint32_t spl
   const uint32_t per_row = 2 * splits;
   const uint64_t p = lane < per_row ? partials[(uint64_t)row * per_row + lane] : 0;
   const bool in0 = lane < splits;
-  uint32_t a1 = in0 ? (uint32_t)(p >> 32) : 0, a2 = in0 ? (uint32_t)p : 0;
-  uint32_t b1 = in0 ? 0 : (uint32_t)(p >> 32), b2 = in0 ? 0 : (uint32_t)p;
-  wave_reduce(a1, a2);
-  wave_reduce(b1, b2);
+  // Widen the slice's keys: the column within the shard is the slice start
+  // plus the column within the slice.
+  const uint32_t c0 = (in0 ? lane : lane - splits) * sh.slice[in0 ? 0 : 1];
+  auto widen = [&](uint32_t k) -> uint64_t {
+    if (k == 0) return 0;
+    const uint32_t col = c0 + (0xFFFFu - (k & 0xFFFFu));
+    return ((uint64_t)(k >> 16) << 32) | (0xFFFFFFFFu - col);
+  };
+  const uint64_t w1 = lane < per_row ? widen((uint32_t)(p >> 32)) : 0;
+  const uint64_t w2 = lane < per_row ? widen((uint32_t)p) : 0;
+  uint64_t a1 = in0 ? w1 : 0, a2 = in0 ? w2 : 0;
+  uint64_t b1 = in0 ? 0 : w1, b2 = in0 ? 0 : w2;
+  wave_reduce64(a1, a2);
+  wave_reduce64(b1, b2);
   if (lane != 63) return;
 
   // Shard records -> global order (ord desc, global id asc).
@@ -202,11 +245,11 @@ __global__ __launch_bounds__(64) void argmax_fold_kernel(Shards sh, uint32_t spl
     uint32_t col;
     bool has;
   };
-  auto rec = [&](uint32_t key, uint32_t shard) {
+  auto rec = [&](uint64_t key, uint32_t shard) {
     Rec r;
     r.has = key != 0;
-    r.ord = key >> 16;
-    r.col = 0xFFFFu - (key & 0xFFFFu);
+    r.ord = (uint32_t)(key >> 32);
+    r.col = 0xFFFFFFFFu - (uint32_t)key;
     r.gid = sh.off[shard] + r.col;
     r.shard = shard;
     return r;
@@ -259,8 +302,11 @@ uint32_t argmax_splits(uint32_t rows, uint32_t ncols0, uint32_t ncols1) {
   uint64_t want = (kTargetWorkgroups + 2ull * rows - 1) / (2ull * rows);
   const uint64_t by_width = (widest + kMinSliceCols - 1) / kMinSliceCols;
   if (want > by_width) want = by_width;
-  if (want > kMaxSplits) want = kMaxSplits;
+  if (want > kArgmaxMaxSplits) want = kArgmaxMaxSplits;
   if (want < 1) want = 1;
+  // no slice wider than kArgmaxMaxSliceCols (the 16-bit column of a key)
+  const uint64_t need = ((uint64_t)widest + kArgmaxMaxSliceCols - 1) / kArgmaxMaxSliceCols;
+  if (want < need) want = need;  // more than kArgmaxMaxSplits: the host refuses the call
   return (uint32_t)want;
 }
 

@@ -117,6 +117,11 @@ struct ArgmaxShard {
   uint32_t ncols;
   uint32_t col_offset;
 };
+// Column slices per shard (the fold's wavefront holds 2 * splits partials) and
+// the widest slice (a key carries a 16-bit column within its slice).
+constexpr uint32_t kArgmaxMaxSplits = 32;
+constexpr uint32_t kArgmaxMaxSliceCols = 65536;
+constexpr uint64_t kArgmaxMaxShardCols = (uint64_t)kArgmaxMaxSplits * kArgmaxMaxSliceCols;
 uint32_t argmax_splits(uint32_t rows, uint32_t ncols0, uint32_t ncols1);
 uint64_t argmax_workspace_bytes(uint32_t rows, uint32_t splits);
 hipError_t launch_argmax(ArgmaxShard s0, ArgmaxShard s1, uint32_t rows, int mode, void *out, void *workspace,

@@ -159,7 +159,7 @@ typedef struct {
   const uint16_t *ptr; /* (device) element (0, 0) of the shard             */
   size_t ld;           /* elements between the starts of consecutive rows  */
   uint32_t rows;
-  uint32_t ncols;      /* 1 .. 65536                                       */
+  uint32_t ncols;      /* 1 .. 2,097,152                                   */
   uint32_t col_offset; /* global id of the shard's column 0                */
 } xfer_shard;
 
@@ -200,8 +200,8 @@ typedef struct {
  * be multiples of 16), different row counts, ncols == 0, shards whose id
  * ranges overlap, col_offset + ncols > 2^31, an unknown mode, a small
  * workspace, or an output overlapping the logits or the workspace;
- * XFER_E_UNSUPPORTED for a shard wider than 65536 columns or more than
- * 2^23 - 1 rows.
+ * XFER_E_UNSUPPORTED for a shard wider than 2,097,152 columns (32 slices of
+ * at most 65,536) or more than 2^23 - 1 rows.
  */
 XFER_API size_t xfer_argmax_workspace_bytes(uint32_t rows, uint32_t ncols0, uint32_t ncols1);
 XFER_API int xfer_argmax_merge(const xfer_shard *s0, const xfer_shard *s1, int mode, void *out, void *workspace,
@@ -225,8 +225,9 @@ XFER_API int xfer_argmax_merge(const xfer_shard *s0, const xfer_shard *s1, int m
  *
  * Arguments, outputs and errors as xfer_argmax_merge without the workspace,
  * plus XFER_E_UNSUPPORTED when the partial records need more than
- * XFER_ARGMAX_SCRATCH_BYTES (xfer_argmax_workspace_bytes above it: more than
- * 4096 rows), and XFER_E_DEVICE if the array's address cannot be obtained.
+ * XFER_ARGMAX_SCRATCH_BYTES (xfer_argmax_workspace_bytes above it: with
+ * shards of at most 65,536 columns, more than 4096 rows), and XFER_E_DEVICE
+ * if the array's address cannot be obtained.
  */
 #define XFER_ARGMAX_SCRATCH_BYTES 65536
 XFER_API int xfer_argmax_merge_noalloc(const xfer_shard *s0, const xfer_shard *s1, int mode, void *out,

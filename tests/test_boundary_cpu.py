@@ -108,7 +108,14 @@ def test_argmax_argument_checks():
     assert f(s0, _sh(ncols=0, off=512)) == x.E_INVAL              # empty shard
     assert f(s0, _sh(off=100, ptr=0x100400)) == x.E_INVAL         # id ranges overlap
     assert f(s0, _sh(off=(1 << 31) - 10, ptr=0x100400)) == x.E_INVAL  # ids past 2^31
-    assert f(_sh(ncols=70000, ld=70000), _sh(off=70000, ptr=0x200000)) == x.E_UNSUPPORTED
+    wide = 32 * 65536                                             # 32 slices of 65,536 columns
+    assert f(_sh(ncols=wide + 1, ld=wide + 8), _sh(off=wide + 1, ptr=1 << 34), out=1 << 36, ws=1 << 37) \
+        == x.E_UNSUPPORTED
+    assert f(_sh(ncols=wide, ld=wide), _sh(off=wide, ptr=1 << 34), out=1 << 36, ws=1 << 37, wsb=16) \
+        == x.E_INVAL                                              # the widest shard passes, then the workspace is short
+    assert x.argmax_workspace_bytes(4, wide, 1) == 4 * 2 * 32 * 8  # 32 slices per shard
+    assert x.argmax_workspace_bytes(4096, 65536, 1) == 4096 * 2 * 1 * 8  # many rows: one slice per shard
+    assert x.argmax_workspace_bytes(4096, 65537, 1) == 4096 * 2 * 2 * 8  # a slice holds at most 65,536 columns
     assert f(_sh(ptr=0x100002), s1) == x.E_INVAL                  # misaligned shard
     assert f(_sh(ld=1001), s1) == x.E_INVAL                       # row stride not 16 B
     assert f(_sh(ld=256), s1) == x.E_INVAL                        # rows overlap (ld < ncols)
@@ -131,7 +138,8 @@ def test_argmax_noalloc_argument_checks():
     assert f(s0, _sh(rows=3, off=512, ptr=0x100400)) == x.E_INVAL
     assert f(_sh(rows=0), _sh(rows=0, off=512), out=0) == x.OK    # no rows: empty work
     assert f(s0, _sh(off=100, ptr=0x100400)) == x.E_INVAL
-    assert f(_sh(ncols=70000, ld=70000), _sh(off=70000, ptr=0x200000)) == x.E_UNSUPPORTED
+    assert f(_sh(ncols=32 * 65536 + 1, ld=32 * 65536 + 8), _sh(off=32 * 65536 + 1, ptr=1 << 34),
+             out=1 << 36) == x.E_UNSUPPORTED
     assert f(s0, s1, out=0) == x.E_INVAL
     assert f(s0, s1, out=0x900008) == x.E_INVAL                   # misaligned output
     assert f(s0, s1, out=0x100000 + 64) == x.E_INVAL              # out inside the logits

@@ -91,6 +91,11 @@ ODD = [
     (2, 3, 65536, 8),
     (33, 2049, 4095, 0),
     (64, 64768, 64512, 0),
+    # shards wider than one 65,536-column slice: the slices' keys are widened in the fold
+    (4, 75968, 75968, 0),
+    (3, 70001, 131073, 8),
+    (600, 65537, 9, 0),          # many rows: two slices of the wide shard, one of the narrow
+    (1, 2097152, 5, 0),          # the widest shard: 32 slices of 65,536
 ]
 
 
