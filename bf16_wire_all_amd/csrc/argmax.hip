@@ -16,15 +16,16 @@
 // the counter updates of a row's workgroups serialise, and an agent-scope
 // release in every workgroup writes back L2.)
 //
-// Keys: inside a slice an element is the 32-bit key
-//     ord(value) << 16 | (0xFFFF - column within the slice)
+// Keys: an element is the 32-bit key
+//     ord(value) << 16 | (0xFFFF - column)
 // where ord maps BF16 bit patterns to 16-bit integers in numeric order with
-// -0 and +0 equal (0x8000 +- magnitude).  A larger key is earlier in the
-// row order (larger value, then lower id), keys are unique per slice, and 0
-// (below every finite value and -inf) marks "no element".  A slice is at most
-// 65,536 columns wide, so a shard of up to 32 slices may hold 2,097,152.  The
-// fold widens a slice's keys to 64 bits, ord << 32 | (0xFFFFFFFF - column
-// within the shard), which orders elements of different slices the same way.
+// -0 and +0 equal (0x8000 +- magnitude), and the column counts from the shard
+// start when the shard holds at most 65,536 columns.  A larger key is earlier
+// in the row order (larger value, then lower id), and 0 (below every finite
+// value and -inf) marks "no element".  A wider shard (up to 32 slices of at
+// most 65,536 columns: 2,097,152) counts key columns from the slice start,
+// and the fold widens each slice's keys to 64 bits, ord << 32 | (0xFFFFFFFF -
+// column within the shard), before comparing keys of different slices.
 // The first two elements of any set follow from the pairwise merge
 //     top1 = max(x1, y1), top2 = max(min(x1, y1), max(x2, y2)).
 // The wavefront reductions use DPP lane moves.
@@ -162,6 +163,10 @@ struct Shards {
 };
 
 // Workgroup (row, shard s, slice k) -> partials[blockIdx.x] = (top1 << 32 | top2).
+// WIDE: a shard is wider than one 65,536-column slice, and key columns count
+// from the slice start; otherwise from the shard start (keys of different
+// slices then compare directly).
+template <bool WIDE>
 __global__ __launch_bounds__(kThreads) void argmax_scan_kernel(Shards sh, uint32_t splits, uint64_t *partials) {
   const uint32_t per_row = 2 * splits;
   const uint32_t row = blockIdx.x / per_row;
@@ -181,19 +186,20 @@ __global__ __launch_bounds__(kThreads) void argmax_scan_kernel(Shards sh, uint32
   const uint32_t n_vec = (c1 - c0) / 8;
   const v4u *vp = reinterpret_cast<const v4u *>(rowp + c0);
   uint32_t v = tid;
-  // Columns are counted from the slice start (c1 - c0 <= 65,536).
+  // Key columns count from `base` (c1 - base <= 65,536 either way).
+  const uint32_t base = WIDE ? c0 : 0;
   for (; v + kThreads < n_vec; v += 2 * kThreads) {
     const v4u w0 = __builtin_nontemporal_load(&vp[v]);
     const v4u w1 = __builtin_nontemporal_load(&vp[v + kThreads]);
-    take8(t1, t2, w0, 8 * v);
-    take8(t1, t2, w1, 8 * (v + kThreads));
+    take8(t1, t2, w0, c0 - base + 8 * v);
+    take8(t1, t2, w1, c0 - base + 8 * (v + kThreads));
   }
-  for (; v < n_vec; v += kThreads) take8(t1, t2, __builtin_nontemporal_load(&vp[v]), 8 * v);
+  for (; v < n_vec; v += kThreads) take8(t1, t2, __builtin_nontemporal_load(&vp[v]), c0 - base + 8 * v);
   // Columns past the last whole vector (only in a shard's last slice).
   const uint32_t c_tail = c0 + 8 * n_vec;
   if (tid < c1 - c_tail) {
     const uint32_t c = c_tail + tid;
-    take(t1, t2, (ord16(rowp[c]) << 16) | (0xFFFFu - (c - c0)));
+    take(t1, t2, (ord16(rowp[c]) << 16) | (0xFFFFu - (c - base)));
   }
 
   wave_reduce(t1, t2);
@@ -213,28 +219,45 @@ __global__ __launch_bounds__(kThreads) void argmax_scan_kernel(Shards sh, uint32
 }
 
 // One wavefront per row: lane i holds partial i of the row; lanes
-// [0, splits) are shard 0's slices, [splits, 2 * splits) shard 1's.
-template <int MODE>
+// [0, splits) are shard 0's slices, [splits, 2 * splits) shard 1's.  Each
+// shard's top two end as 64-bit keys ord << 32 | (0xFFFFFFFF - column within
+// the shard).
+template <int MODE, bool WIDE>
 __global__ __launch_bounds__(64) void argmax_fold_kernel(Shards sh, uint32_t splits, const uint64_t *partials,
                                                          void *out) {
   const uint32_t row = blockIdx.x, lane = threadIdx.x;
   const uint32_t per_row = 2 * splits;
   const uint64_t p = lane < per_row ? partials[(uint64_t)row * per_row + lane] : 0;
   const bool in0 = lane < splits;
-  // Widen the slice's keys: the column within the shard is the slice start
-  // plus the column within the slice.
-  const uint32_t c0 = (in0 ? lane : lane - splits) * sh.slice[in0 ? 0 : 1];
-  auto widen = [&](uint32_t k) -> uint64_t {
+  // A 32-bit key with its column counted from `c0` -> the 64-bit key.
+  auto widen = [](uint32_t k, uint32_t c0) -> uint64_t {
     if (k == 0) return 0;
     const uint32_t col = c0 + (0xFFFFu - (k & 0xFFFFu));
     return ((uint64_t)(k >> 16) << 32) | (0xFFFFFFFFu - col);
   };
-  const uint64_t w1 = lane < per_row ? widen((uint32_t)(p >> 32)) : 0;
-  const uint64_t w2 = lane < per_row ? widen((uint32_t)p) : 0;
-  uint64_t a1 = in0 ? w1 : 0, a2 = in0 ? w2 : 0;
-  uint64_t b1 = in0 ? 0 : w1, b2 = in0 ? 0 : w2;
-  wave_reduce64(a1, a2);
-  wave_reduce64(b1, b2);
+  uint64_t a1, a2, b1, b2;
+  if (WIDE) {
+    // keys of different slices compare only once widened with the slice start
+    const uint32_t c0 = (in0 ? lane : lane - splits) * sh.slice[in0 ? 0 : 1];
+    const uint64_t w1 = lane < per_row ? widen((uint32_t)(p >> 32), c0) : 0;
+    const uint64_t w2 = lane < per_row ? widen((uint32_t)p, c0) : 0;
+    a1 = in0 ? w1 : 0;
+    a2 = in0 ? w2 : 0;
+    b1 = in0 ? 0 : w1;
+    b2 = in0 ? 0 : w2;
+    wave_reduce64(a1, a2);
+    wave_reduce64(b1, b2);
+  } else {
+    // shard-relative 32-bit keys compare directly; widen the shard's result
+    uint32_t x1 = in0 ? (uint32_t)(p >> 32) : 0, x2 = in0 ? (uint32_t)p : 0;
+    uint32_t y1 = in0 ? 0 : (uint32_t)(p >> 32), y2 = in0 ? 0 : (uint32_t)p;
+    wave_reduce(x1, x2);
+    wave_reduce(y1, y2);
+    a1 = widen(x1, 0);
+    a2 = widen(x2, 0);
+    b1 = widen(y1, 0);
+    b2 = widen(y2, 0);
+  }
   if (lane != 63) return;
 
   // Shard records -> global order (ord desc, global id asc).
@@ -325,12 +348,20 @@ hipError_t launch_argmax(ArgmaxShard s0, ArgmaxShard s1, uint32_t rows, int mode
     sh.slice[i] = round_up8((in[i].ncols + splits - 1) / splits);
   }
   uint64_t *partials = reinterpret_cast<uint64_t *>(workspace);
-  hipError_t e = launch(argmax_scan_kernel, dim3(rows * 2 * splits), dim3(kThreads), 0, stream, sh, splits, partials);
-  if (e != hipSuccess) return e;
   const uint64_t *cp = partials;
+  const dim3 scan_grid(rows * 2 * splits), fold_grid(rows);
+  if (s0.ncols > kArgmaxMaxSliceCols || s1.ncols > kArgmaxMaxSliceCols) {
+    hipError_t e = launch(argmax_scan_kernel<true>, scan_grid, dim3(kThreads), 0, stream, sh, splits, partials);
+    if (e != hipSuccess) return e;
+    if (mode == XFER_ARGMAX)
+      return launch(argmax_fold_kernel<XFER_ARGMAX, true>, fold_grid, dim3(64), 0, stream, sh, splits, cp, out);
+    return launch(argmax_fold_kernel<XFER_TOP2, true>, fold_grid, dim3(64), 0, stream, sh, splits, cp, out);
+  }
+  hipError_t e = launch(argmax_scan_kernel<false>, scan_grid, dim3(kThreads), 0, stream, sh, splits, partials);
+  if (e != hipSuccess) return e;
   if (mode == XFER_ARGMAX)
-    return launch(argmax_fold_kernel<XFER_ARGMAX>, dim3(rows), dim3(64), 0, stream, sh, splits, cp, out);
-  return launch(argmax_fold_kernel<XFER_TOP2>, dim3(rows), dim3(64), 0, stream, sh, splits, cp, out);
+    return launch(argmax_fold_kernel<XFER_ARGMAX, false>, fold_grid, dim3(64), 0, stream, sh, splits, cp, out);
+  return launch(argmax_fold_kernel<XFER_TOP2, false>, fold_grid, dim3(64), 0, stream, sh, splits, cp, out);
 }
 
 }  // namespace xfer
