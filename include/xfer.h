@@ -14,8 +14,11 @@
  * Conventions shared by every call:
  *   - Pointers marked (device) are device addresses of the GPU that is current
  *     on the calling thread; pointers marked (host) are host memory.  The
- *     caller owns every buffer, including the run plans; the library keeps no
- *     global state and allocates no device memory.
+ *     caller owns every buffer, including the run plans.  The library
+ *     allocates no device memory itself; its only global state is the static
+ *     partials array of xfer_argmax_merge_noalloc (one per GPU) and the cache
+ *     of its addresses.  xfer_allreduce2_graph_create creates HIP graph
+ *     objects, which the caller frees with xfer_allreduce2_graph_destroy.
  *   - Hot calls (pack, combine, argmax, gather, scatter, the descriptor and
  *     paged copies) only enqueue work on `stream`: they never allocate, never
  *     synchronise and never block.  The set-up calls that upload a plan
