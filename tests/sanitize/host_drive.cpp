@@ -553,6 +553,60 @@ void staging_spans() {
     bad.spans[3] = bad.spans[2];
     CHECK(xfer_copy_descs(&bad, arena.p + 8 * U, 6 * U, token(9)) == XFER_E_INVAL);
   }
+  // random region sets: at most four sorted, disjoint spans that cover every
+  // segment byte, inside [span_lo, span_hi), each starting and ending on a segment
+  {
+    Rng g{0x5BA45ull};
+    for (int it = 0; it < 200; ++it) {
+      const uint32_t nr = 1 + (uint32_t)g.below(9), L = 1 + (uint32_t)g.below(12);
+      std::vector<uint64_t> roff(nr);
+      uint64_t at = 0;
+      for (uint32_t r = 0; r < nr; ++r) {
+        roff[r] = at;
+        at += 4 + g.below(6) + g.below(2) * g.below(40);  // region of 4 units, then a gap of 0..50
+      }
+      Buf ar((at + 4) * 64);
+      std::vector<xfer_region> rr(nr);
+      for (uint32_t r = 0; r < nr; ++r) rr[r] = xfer_region{ar.addr() + roff[r] * 64, 4 * 64};
+      std::vector<uint32_t> rp(L, 1), ct(L, 1);
+      std::vector<uint64_t> bs(L);
+      std::vector<int64_t> sd(L, 0);
+      std::vector<bool> used(4 * nr, false);
+      for (uint32_t l = 0; l < L; ++l) {  // one 64-byte segment per lane, in a random free slot
+        uint64_t k;
+        do k = g.below(4 * nr); while (used[k]);
+        if ((uint64_t)std::count(used.begin(), used.end(), true) + 1 >= 4 * nr) break;
+        used[k] = true;
+        bs[l] = rr[k / 4].base + (k % 4) * 64;
+      }
+      const uint32_t Lu = (uint32_t)std::count(used.begin(), used.end(), true);
+      if (Lu == 0) continue;
+      bs.resize(Lu);
+      xfer_run_table rt{Lu, 1, 64, Lu, rp.data(), bs.data(), sd.data(), ct.data()};
+      Buf rdev(xfer_runs_plan_bytes(&rt));
+      xfer_runs_plan pl;
+      CHECK(xfer_runs_prepare(&rt, rr.data(), (int)nr, 0, rdev.p, rdev.n, &pl) == XFER_OK);
+      CHECK(pl.n_spans >= 1 && pl.n_spans <= 4);
+      for (uint32_t i = 0; i < pl.n_spans; ++i) {
+        CHECK(pl.spans[2 * i] < pl.spans[2 * i + 1]);
+        if (i) CHECK(pl.spans[2 * i - 1] < pl.spans[2 * i]);  // sorted, disjoint, not touching
+      }
+      CHECK(pl.spans[0] == pl.span_lo && pl.spans[2 * pl.n_spans - 1] == pl.span_hi);
+      for (uint32_t l = 0; l < Lu; ++l) {  // every segment inside one span
+        bool in = false;
+        for (uint32_t i = 0; i < pl.n_spans && !in; ++i) in = bs[l] >= pl.spans[2 * i] && bs[l] + 64 <= pl.spans[2 * i + 1];
+        CHECK(in);
+      }
+      for (uint32_t i = 0; i < pl.n_spans; ++i) {  // every span starts and ends on a segment
+        bool lo = false, hi = false;
+        for (uint32_t l = 0; l < Lu; ++l) {
+          lo = lo || bs[l] == pl.spans[2 * i];
+          hi = hi || bs[l] + 64 == pl.spans[2 * i + 1];
+        }
+        CHECK(lo && hi);
+      }
+    }
+  }
   // two regions: the whole range between them is free for staging
   xfer_run_table t2{2, 1, U, 2, rpl.data(), base.data(), stride.data(), cnt.data()};
   Buf dev2(xfer_runs_plan_bytes(&t2));
