@@ -1,7 +1,9 @@
 """The C ABI seen from plain C: include/xfer.h compiles as C11 with gcc, a C
-program links libxfer.so and calls host-only entry points, and every struct
-size and field offset the C compiler lays out equals the Python binding's
-ctypes (and numpy) layout, so no call reads a field at the wrong place."""
+program links libxfer.so and calls host-only entry points, every struct size
+and field offset the C compiler lays out equals the Python binding's ctypes
+(and numpy) layout, and every exported call's parameter list in the header
+matches the binding's argtypes and restype in count, width and signedness,
+so no call reads an argument or a field at the wrong place or width."""
 import ctypes
 import os
 import shutil
@@ -80,3 +82,56 @@ def test_host_calls_from_c_match_python(layout):
     st, n_deps = (int(v) for v in calls["graph_deps"])
     assert (st, n_deps) == (x.E_RANGE, len(x.allreduce2_graph_deps(3, 2)))
     assert calls["status"] == ["named"]
+
+
+def _decls():
+    """(name, return type, [parameter types]) of every XFER_API declaration."""
+    import re
+    src = open(os.path.join(ROOT, "include", "xfer.h")).read()
+    out = []
+    for ret, args in re.findall(r"XFER_API\s+([^;]*?)\s*\(([^)]*)\)\s*;", src, re.S):
+        ret = " ".join(ret.split())
+        m = re.match(r"(.*?)(\w+)$", ret)
+        params = []
+        for a in " ".join(args.split()).split(","):
+            a = a.strip()
+            if a and a != "void":
+                params.append(re.match(r"(.*?)\w+$", a).group(1).replace("const ", "").replace(" ", ""))
+        out.append((m.group(2), m.group(1).replace("const ", "").replace(" ", ""), params))
+    return out
+
+
+SCALARS = {"int": ctypes.c_int, "uint32_t": ctypes.c_uint32, "uint64_t": ctypes.c_uint64,
+           "size_t": ctypes.c_size_t, "int64_t": ctypes.c_int64}
+STRUCTS = {"xfer_shard*": x.Shard, "xfer_run_table*": x.RunTableC, "xfer_region*": x.Region,
+           "xfer_runs_plan*": x.RunsPlan, "xfer_descs_plan*": x.DescsPlan, "xfer_pages*": x.PagesC,
+           "xfer_pages_plan*": x.PagesPlan, "xfer_op*": x.Op, "xfer_allreduce2_desc*": x.AllReduce2Desc}
+HANDLES = {"hipStream_t", "hipGraphExec_t"}          # opaque pointers passed by value
+
+
+def _compatible(c_type, py):
+    if c_type in SCALARS:
+        return py is SCALARS[c_type]
+    if c_type in STRUCTS:
+        return py is ctypes.c_void_p or py is ctypes.POINTER(STRUCTS[c_type])
+    if c_type == "hipGraphExec_t*":
+        return py is ctypes.POINTER(ctypes.c_void_p)
+    if c_type.endswith("*") or c_type in HANDLES:
+        return py is ctypes.c_void_p or (isinstance(py, type) and issubclass(py, ctypes._Pointer))
+    return False
+
+
+def test_every_exported_signature_matches_the_binding():
+    """Argument count, width and signedness of every exported call as the
+    binding declares it (ctypes argtypes / restype) equal the header's."""
+    L = x.lib()
+    decls = _decls()
+    assert sorted(d[0] for d in decls) == sorted(x.EXPORTED)
+    for name, ret, params in decls:
+        fn = getattr(L, name)
+        assert len(fn.argtypes) == len(params), name
+        for i, (c_type, py) in enumerate(zip(params, fn.argtypes)):
+            assert _compatible(c_type, py), (name, i, c_type, py)
+        want_ret = {"int": ctypes.c_int, "size_t": ctypes.c_size_t, "uint32_t": ctypes.c_uint32,
+                    "char*": ctypes.c_char_p}[ret]
+        assert fn.restype is want_ret, (name, ret, fn.restype)
