@@ -10,7 +10,7 @@ import torch
 import bf16_wire_all_amd as x
 import datagen as dg
 import oracle
-from tests.gpu_util import DEV, down, filled, random_bf16, random_f32_bits, say, up, zeros
+from tests.gpu_util import down, filled, random_bf16, random_f32_bits, say, up, zeros
 
 pytestmark = pytest.mark.gpu
 

@@ -11,7 +11,7 @@ import torch
 import bf16_wire_all_amd as x
 import datagen as dg
 import oracle
-from tests.gpu_util import DEV, down, filled, say, up, zeros
+from tests.gpu_util import down, filled, say, up, zeros
 
 pytestmark = pytest.mark.gpu
 

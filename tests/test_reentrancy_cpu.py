@@ -5,7 +5,6 @@ encoder, table validation, the coalescing planner, the streamed schedule and
 the graph form's dependency list; none of them may keep state between calls."""
 from concurrent.futures import ThreadPoolExecutor
 
-import numpy as np
 
 import bf16_wire_all_amd as x
 import datagen as dg
