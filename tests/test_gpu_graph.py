@@ -1,7 +1,8 @@
 """Every hot call can be captured in a HIP graph: the calls only enqueue
 kernels on the given stream (no allocation, no synchronisation, no memset).
 A whole step (both packs, combine2 in both modes, combine2_f32, argmax_merge,
-gather, scatter, the coalesced fetch and a paged copy) is captured once and
+argmax_merge_noalloc (the form for callers that cannot allocate, e.g. under
+capture), gather, scatter, the coalesced fetch and a paged copy) is captured once and
 replayed three times, with the inputs rewritten by eager work between the
 replays; after every replay each output must equal the oracle on that
 replay's inputs, bit for bit."""
@@ -34,6 +35,7 @@ def test_captured_step_replays_bit_exact():
     logits = zeros(2 * rows * cols)
     ws = zeros(x.argmax_workspace_bytes(rows, split, cols - split))
     top2 = zeros(16 * rows)
+    max_noalloc = zeros(8 * rows)
     regs = [zeros(rb) for _ in range(2)]
     bases = [r.data_ptr() for r in regs]
     regions = [(p, rb) for p in bases]
@@ -67,6 +69,7 @@ def test_captured_step_replays_bit_exact():
         x.combine2_f32(fa, fb, f32w_f32.view(torch.float32), x.OUT_F32)
         x.combine2_f32(fa, fb, f32w_b16.view(torch.int16), x.OUT_BF16)
         x.argmax_merge(s0, s1, x.TOP2, top2, ws)
+        x.argmax_merge_noalloc(s0, s1, x.ARGMAX, max_noalloc)
         x.gather_runs(splan, staging)
         x.scatter_runs(staging, dplan)
         x.copy_descs(fplan, slab)
@@ -120,6 +123,7 @@ def test_captured_step_replays_bit_exact():
         assert np.array_equal(down(f32w_f32, np.uint32), oracle.combine2_f32(ha, hb, 0)), k
         assert np.array_equal(down(f32w_b16, np.uint16), oracle.combine2_f32(ha, hb, 1)), k
         assert down(top2).tobytes() == oracle.argmax_merge(lg, split, x.TOP2).tobytes(), k
+        assert down(max_noalloc).tobytes() == oracle.argmax_merge(lg, split, x.ARGMAX).tobytes(), k
         oregions = list(zip(bases, hosts))
         want_stage = oracle.gather(ot, seg, oregions)
         assert np.array_equal(down(staging), want_stage), k
