@@ -39,22 +39,36 @@ int xfer_pages_prepare(uint64_t page_len, const xfer_region *src, const xfer_pag
       return XFER_E_INVAL;
     if (!aligned16(src->base) || !aligned16(dst->base)) return XFER_E_INVAL;
     if (src->base > UINT64_MAX - src->bytes || dst->base > UINT64_MAX - dst->bytes) return XFER_E_INVAL;
-    if (src->base < dst->base + dst->bytes && dst->base < src->base + src->bytes) return XFER_E_INVAL;
+    const bool regions_overlap = src->base < dst->base + dst->bytes && dst->base < src->base + src->bytes;
     const uint64_t upp = (page_len + xfer::kPageUnitBytes - 1) / xfer::kPageUnitBytes;
     if (upp > UINT32_MAX || (n_pages && n_pages > UINT32_MAX / upp)) return XFER_E_UNSUPPORTED;
     const uint64_t n_units = n_pages * upp;
     if (xfer::paired_pieces(n_units) > xfer::kMaxGridBlocks) return XFER_E_UNSUPPORTED;
-    std::vector<uint64_t> starts(n_pages);
+    // Page starts as device addresses (each region lies below 2^64, checked above).
+    std::vector<uint64_t> starts(n_pages), src_starts(regions_overlap ? n_pages : 0);
     for (uint64_t k = 0; k < n_pages; ++k) {
       uint64_t s, d;
       if (!page_at(sp->indices[k], *sp, page_len, src->bytes, &s) ||
           !page_at(dp->indices[k], *dp, page_len, dst->bytes, &d))
         return XFER_E_RANGE;
-      starts[k] = d;
+      starts[k] = dst->base + d;
+      if (regions_overlap) src_starts[k] = src->base + s;
     }
     std::sort(starts.begin(), starts.end());
     for (uint64_t k = 1; k < n_pages; ++k)
       if (starts[k] - starts[k - 1] < page_len) return XFER_E_OVERLAP;
+    // The regions may overlap (or be one region): then no destination page may
+    // share a byte with a source page, or the result would depend on the order
+    // of the copies.  Both lists sorted; each destination page against its
+    // nearest source pages below and above.
+    if (regions_overlap) {
+      std::sort(src_starts.begin(), src_starts.end());
+      for (uint64_t d : starts) {
+        const auto it = std::lower_bound(src_starts.begin(), src_starts.end(), d);
+        if (it != src_starts.end() && *it - d < page_len) return XFER_E_OVERLAP;
+        if (it != src_starts.begin() && d - *(it - 1) < page_len) return XFER_E_OVERLAP;
+      }
+    }
     const uint64_t need = xfer_pages_plan_bytes(n_pages);
     if (n_pages && (!dev || !aligned16((uintptr_t)dev) || dev_bytes < need)) return XFER_E_INVAL;
     const uint64_t half = up16(n_pages * sizeof(uint32_t));

@@ -499,14 +499,16 @@ XFER_API size_t xfer_pages_plan_bytes(uint64_t n_pages);
  * this order:
  *   XFER_E_INVAL  NULL out, regions or page lists (with n_pages > 0), a
  *                 page_len that is 0 or not a multiple of 16, a stride,
- *                 offset or region base not a multiple of 16, a region that
- *                 wraps past 2^64, or source and destination regions that
- *                 overlap;
+ *                 offset or region base not a multiple of 16, or a region
+ *                 that wraps past 2^64;
  *   XFER_E_UNSUPPORTED  more than 2^32 - 1 units of 4 KiB, or a grid above
  *                 2^24 - 1 workgroups;
  *   XFER_E_RANGE  a page (either list) not wholly inside its region, or
  *                 offset arithmetic that overflows 64 bits;
- *   XFER_E_OVERLAP  two destination pages that overlap;
+ *   XFER_E_OVERLAP  two destination pages that overlap, or (when the two
+ *                 regions overlap or are one region, as for a copy within
+ *                 one buffer) a destination page that shares a byte with a
+ *                 source page;
  *   XFER_E_INVAL  dev NULL, misaligned or smaller than
  *                 xfer_pages_plan_bytes(n_pages);
  *   XFER_E_DEVICE  the upload failed.

@@ -324,6 +324,38 @@ void pages(Rng &g) {
   }
 }
 
+// A paged copy inside one buffer: accepted while no destination page shares a
+// byte with a source page, refused (XFER_E_OVERLAP) once one does.
+void pages_in_one_region(Rng &g) {
+  const uint64_t page = 256, slots = 64;
+  Buf buf(slots * page);
+  const xfer_region r{buf.addr(), buf.n};
+  for (int it = 0; it < 100; ++it) {
+    const uint64_t n = 1 + g.below(slots / 2);
+    std::vector<uint32_t> perm(slots);
+    std::iota(perm.begin(), perm.end(), 0u);
+    for (uint64_t i = slots; i > 1; --i) std::swap(perm[i - 1], perm[g.below(i)]);
+    std::vector<uint32_t> si(perm.begin(), perm.begin() + n), di(perm.begin() + n, perm.begin() + 2 * n);
+    const bool clash = g.below(2) == 1;
+    if (clash) di[g.below(n)] = si[g.below(n)];  // one destination page is also a source page
+    const xfer_pages sp{si.data(), page, 0}, dp{di.data(), page, 0};
+    Buf dev(xfer_pages_plan_bytes(n));
+    xfer_pages_plan plan;
+    const int st = xfer_pages_prepare(page, &r, &sp, &r, &dp, n, dev.p, dev.n, &plan);
+    CHECK(st == (clash ? XFER_E_OVERLAP : XFER_OK));
+    if (st == XFER_OK) CHECK(xfer_paged_copy(&plan, token(6)) == XFER_OK);
+    // the same lists shifted by a few bytes of offset: pages straddle, still disjoint or not
+    const xfer_pages dp16{di.data(), page, 16};
+    if (!clash && di.size() && *std::max_element(di.begin(), di.end()) < slots - 1) {
+      bool touch = false;
+      for (uint32_t a : si)
+        for (uint32_t b : di) touch = touch || a == b + 1;  // page b shifted by 16 bytes runs into page b + 1
+      CHECK(xfer_pages_prepare(page, &r, &sp, &r, &dp16, n, dev.p, dev.n, &plan) ==
+            (touch ? XFER_E_OVERLAP : XFER_OK));
+    }
+  }
+}
+
 void streamed(Rng &g) {
   for (uint32_t R = 1; R <= 4; ++R)
     for (uint32_t nc = 0; nc < 10; ++nc) {
@@ -702,6 +734,7 @@ int main() {
   statuses();
   pack_combine(g);
   staging_spans();
+  pages_in_one_region(g);
   argmax(g);
   runs_and_groups(g);
   pages(g);

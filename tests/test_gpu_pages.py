@@ -110,3 +110,33 @@ def test_refused_prepare_writes_nothing():
                                    (dst.data_ptr(), dst.numel()), [1, 1], 4096, 0, dev.data_ptr(), 256)
     assert st == x.E_OVERLAP
     assert np.all(down(dst) == 0x22) and np.all(down(dev) == 0)
+
+
+@pytest.mark.parametrize("page_len,n", [(4096, 300), (272, 41), (65536, 9)])
+def test_copy_within_one_buffer(page_len, n):
+    """Source and destination pages in one buffer (a compaction: scattered
+    pages moved into a free area of the same allocation).  The prepare
+    accepts it because no destination page shares a byte with a source page;
+    every moved page, and every byte outside the destination pages, matches
+    the oracle run on the same single image."""
+    slots = 3 * n + 5
+    nbytes = 32 + slots * page_len
+    h = dg.random_u64(nbytes // 8 + 1, page_len + n).view(np.uint8)[:nbytes].copy()
+    perm = dg.permutation(slots, 7 * n + page_len)
+    si, di = perm[:n], perm[n:2 * n]
+    buf = up(h)
+    say("paged copy within one buffer", page_len, n)
+    dev = zeros(max(16, x.pages_plan_bytes(n)))
+    region = (buf.data_ptr(), buf.numel())
+    plan = x.pages_prepare(page_len, region, si, page_len, 32, region, di, page_len, 32, dev)
+    x.paged_copy(plan)
+    want = h.copy()
+    oracle.paged_copy(page_len, h, si, page_len, 32, want, di, page_len, 32)
+    assert np.array_equal(down(buf), want)
+    # a destination list that reuses one source page is refused, and nothing is written
+    bad = di.copy()
+    bad[n // 2] = si[0]
+    st, _ = x.pages_prepare_status(page_len, region, si, page_len, 32, region, bad, page_len, 32, dev.data_ptr(),
+                                   dev.numel())
+    assert st == x.E_OVERLAP
+    assert np.array_equal(down(buf), want)

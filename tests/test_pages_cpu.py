@@ -134,7 +134,13 @@ def test_library_checks_in_order():
     assert _prep(ss=4104) == x.E_INVAL                                    # misaligned stride
     assert _prep(do=8) == x.E_INVAL                                       # misaligned offset
     assert _prep(src=(0x10000008, 1 << 20)) == x.E_INVAL                  # misaligned region
-    assert _prep(dst=(0x10080000, 1 << 20)) == x.E_INVAL                  # regions overlap
+    # overlapping regions (or one region) are allowed as long as no destination page touches a source page
+    assert _prep(dst=(0x10080000, 1 << 20)) == x.E_INVAL                  # disjoint pages: then no dev
+    assert _prep(dst=SRC, di=(2, 3)) == x.E_INVAL                         # one region, disjoint pages: no dev
+    assert _prep(dst=SRC, di=(1, 2)) == x.E_OVERLAP                       # page 1 is read and written
+    assert _prep(dst=SRC, di=(2, 3), ds=2048) == x.E_OVERLAP              # destination bytes [4096, 8192) in a source page
+    assert _prep(dst=SRC, si=(4, 5), di=(0, 1), do=64) == x.E_INVAL       # ends 64 bytes short of page 4: no dev
+    assert _prep(dst=SRC, si=(4, 5), di=(3, 4), do=16) == x.E_OVERLAP     # 16 bytes into source page 4
     assert _prep(si=(0, 256)) == x.E_RANGE                                # source page past the end
     assert _prep(di=(255, 256)) == x.E_RANGE                              # destination page past the end
     assert _prep(si=(0, 0xFFFFFFFF), ss=1 << 40) == x.E_RANGE             # offset arithmetic overflows
