@@ -72,6 +72,17 @@ def test_noalloc_largest_then_small_odd_shape():
     _compare(small.logits, 4104)
 
 
+def test_noalloc_wide_shards_then_narrow():
+    """Shards wider than one 65,536-column slice (100,000 and 140,000
+    columns: the 64-bit fold), then a narrow call that reuses the array."""
+    wide = dg.argmax_logits(8, dg.seed_for(3, 0, 10), cols=240000, split=100000)
+    say("noalloc argmax 8 x 240000")
+    _compare(wide.logits, 100000)
+    narrow = dg.argmax_logits(4, dg.seed_for(3, 0, 11), cols=3000, split=1504)
+    say("noalloc argmax 4 x 3000")
+    _compare(narrow.logits, 1504)
+
+
 def test_noalloc_refuses_more_than_the_array_holds():
     rows, cols, split = 4097, 64, 32
     logits = np.zeros((rows, cols), np.uint16)
